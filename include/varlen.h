@@ -1,0 +1,157 @@
+/*
+ * varlen.h -- C ABI of the MI355X (gfx950) packed variable-length attention library.
+ *
+ * All tensor pointers are DEVICE pointers owned by the caller.  Every function
+ * enqueues its work on `stream` and returns at once: no allocation, no
+ * host<->device copy or synchronisation, no global mutable state.  Device-
+ * resident cu_seqlens are trusted preconditions (checking them would need a
+ * device-to-host read); host scalars are validated and a bad one returns an
+ * error code before anything is launched.  Return value: VL_OK (0) on success,
+ * a negative vl_status otherwise.
+ *
+ * Layouts: packed tensors are [T, H, D] row-major (token, head, feature);
+ * block-local tensors are [B, n, H, D]; lse tensors are [T, H] / [B, n, H]
+ * float32, natural log.  Output buffers must not alias inputs.
+ */
+#ifndef VARLEN_MI355X_H
+#define VARLEN_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* vl_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  VL_OK = 0,
+  VL_EINVAL = -1,       /* bad pointer, negative size, misaligned buffer, ... */
+  VL_EUNSUPPORTED = -2, /* a size the kernels do not implement (e.g. head_dim not 64/128) */
+  VL_ELAUNCH = -3       /* the kernel launch itself failed (hipGetLastError after launch) */
+} vl_status;
+
+/* Library version (major*10000 + minor*100 + patch) and a text for a status code. */
+int vl_version(void);
+const char* vl_status_string(int status);
+
+/* ---------------------------------------------------------------- boundaries
+ * cu_seqlens_from_lengths: cu_out[0] = 0, cu_out[r+1] = cu_out[r] + lengths[r].
+ *   Flat varlen attention takes request boundaries as cumulative sequence
+ *   lengths (vLLM-Omni PR #6711, "Key changes": q_cu_seqlens/kv_cu_seqlens).
+ *   lengths: int32 [num_reqs] (device), cu_out: int32 [num_reqs+1] (device).
+ *   0 <= num_reqs <= 65536; the sum must fit in int32 (trusted).
+ *
+ * joint_cu_seqlens: boundaries of a joint [text ; image] packed batch, built
+ *   from the real text mask and the image grids (PR #6711 "Key changes":
+ *   cu_seqlens from real text lengths via mask.sum; PR #4024 "How batching
+ *   works": text lengths from the prompt mask, image grids from img_shapes).
+ *   text_mask: uint8 [num_reqs, text_cap] (nonzero = real token);
+ *   img_hw: int32 [num_reqs, 2] (grid h, w).  Outputs (device, int32):
+ *   cu_joint [num_reqs+1], cu_text [num_reqs+1], cu_img [num_reqs+1] and
+ *   img_dst [num_reqs] = cu_joint[r] + text_len[r] (first packed row of the
+ *   request's image tokens; text precedes image inside a request).
+ *   Any output pointer may be NULL to skip it.
+ */
+int cu_seqlens_from_lengths(const int32_t* lengths, int32_t num_reqs, int32_t* cu_out,
+                            vl_stream_t stream);
+int joint_cu_seqlens(const uint8_t* text_mask, int32_t text_cap, const int32_t* img_hw,
+                     int32_t num_reqs, int32_t* cu_joint, int32_t* cu_text, int32_t* cu_img,
+                     int32_t* img_dst, vl_stream_t stream);
+
+/* ---------------------------------------------------------------- pack / unpack
+ * pack_by_cu_seqlens: copy only the real rows of a padded per-request buffer
+ *   into a flat one (PR #4024 "How batching works": only real tokens are
+ *   packed; padding never enters the attention path).  Request r has
+ *   len_r = cu_seqlens[r+1] - cu_seqlens[r] rows at src_padded + r*max_len rows;
+ *   they go to dst_flat rows dst_row_offsets[r] + i (dst_row_offsets NULL =>
+ *   cu_seqlens[r]).  A row is row_bytes bytes.  Rows of dst no request covers
+ *   are left untouched.  len_r <= max_len is trusted.
+ *
+ * unpack_by_cu_seqlens: the inverse scatter (PR #6711 "Key changes": output
+ *   unpacked by cu_seqlens; PR #4024 "Correctness model": outputs scattered back
+ *   to request-local state): dst_padded[r*max_len + i] = src_flat[off_r + i] for
+ *   i < len_r with off_r = src_row_offsets[r] (NULL => cu_seqlens[r]); rows
+ *   i >= len_r are zeroed when zero_fill != 0, else untouched.
+ *
+ *   Both: row_bytes > 0; 0 <= num_reqs <= 65535; max_len >= 0.  Whole 16-byte
+ *   vectors are used when row_bytes and both base pointers are 16-byte aligned,
+ *   else 4-byte words (row_bytes and pointers 4-byte aligned), else bytes.
+ */
+int pack_by_cu_seqlens(const void* src_padded, int64_t max_len, const int32_t* cu_seqlens,
+                       int32_t num_reqs, int64_t row_bytes, void* dst_flat,
+                       const int32_t* dst_row_offsets, vl_stream_t stream);
+int unpack_by_cu_seqlens(const void* src_flat, const int32_t* src_row_offsets,
+                         const int32_t* cu_seqlens, int32_t num_reqs, int64_t row_bytes,
+                         void* dst_padded, int64_t max_len, int zero_fill, vl_stream_t stream);
+
+/* ---------------------------------------------------------------- varlen attention
+ * varlen_attn_fwd: flat non-causal attention over packed [T, H, D] bf16 Q/K/V
+ *   (PR #6711 "Key changes" and "Reference / Acknowledgement"; PR #4024
+ *   "Correctness model": no token attends across request boundaries).  For
+ *   request r (rows q_cu[r]..q_cu[r+1] of q and kv_cu[r]..kv_cu[r+1] of k/v)
+ *   and head h: out = softmax(scale * Q K^T) V, fp32 accumulation, output
+ *   rounded to bf16 (nearest even); lse = natural-log sum of exp(scale*q.k)
+ *   (fp32, may be NULL).  A request with q_len > 0 and kv_len = 0 gives out = 0
+ *   and lse = -inf.  padded_tokens must be 0: every row of q/k/v belongs to a
+ *   request (there is no argument for padding on purpose).
+ *   q, k, v, out: bf16, 16-byte aligned; q_cu/kv_cu: int32 [num_reqs+1] with
+ *   cu[0] = 0, non-decreasing (trusted).  max_q / max_kv: upper bounds of the
+ *   per-request lengths, used only to size the launch.  D in {64, 128};
+ *   H >= 1; num_reqs >= 0.
+ * varlen_attn_fwd_f32: same contract on float32 q/k/v/out.
+ */
+int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
+                    const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
+                    int32_t H, int32_t D, float scale, void* out, float* lse, vl_stream_t stream);
+int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
+                        const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, int32_t max_q,
+                        int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale,
+                        float* out, float* lse, vl_stream_t stream);
+
+/* ---------------------------------------------------------------- block-local attention
+ * block_local_attn_fwd: the block-local ("block-sparse") attention of the
+ *   Token2Wav DiT (PR #7975, review of the window code, commit messages,
+ *   "Purpose"/"Change"): frames are grouped in blocks of `block`; a query in
+ *   block b attends to every frame j < n whose block lies in
+ *   [b - look_back, b + look_ahead]; no dense n x n mask is formed and only
+ *   the keys of that window are read.  q, k, v, out: bf16 [B, n, H, D];
+ *   lse: fp32 [B, n, H] or NULL.  D in {64, 128}; B, n >= 0; H >= 1;
+ *   block >= 1; look_back, look_ahead >= 0.
+ * block_local_attn_fwd_f32: same contract on float32 tensors.
+ */
+int block_local_attn_fwd(const void* q, const void* k, const void* v, int32_t B, int32_t n,
+                         int32_t H, int32_t D, int32_t block, int32_t look_back,
+                         int32_t look_ahead, float scale, void* out, float* lse,
+                         vl_stream_t stream);
+int block_local_attn_fwd_f32(const float* q, const float* k, const float* v, int32_t B,
+                             int32_t n, int32_t H, int32_t D, int32_t block, int32_t look_back,
+                             int32_t look_ahead, float scale, float* out, float* lse,
+                             vl_stream_t stream);
+
+/* ---------------------------------------------------------------- schedule (test export)
+ * varlen_launch_shape: host-only; the launch varlen_attn_fwd (dtype_f32 = 0)
+ *   or varlen_attn_fwd_f32 (dtype_f32 = 1) uses for these scalars: query rows
+ *   per work-group (block_m), chiplet chunk, and the number of work-groups.
+ *   Any output pointer may be NULL.
+ * varlen_tile_map: writes, for every launched work-group b of that launch, the
+ *   (request, head, q-tile) it computes into triples_out[3*b .. 3*b+2], or
+ *   (-1, -1, -1) for an idle work-group, using the same device code as the
+ *   attention kernel.  triples_out: int32 [max_blocks, 3] (device); max_blocks
+ *   must be >= the launch size, else VL_EINVAL.
+ *   Schedule: requests by key length descending (ties: lower index first) when
+ *   num_reqs <= 64, else in index order; heads ascending; q-tiles ascending.
+ *   Work-group b runs on chiplet b mod 8 and takes logical tile
+ *   ((i div chunk)*8 + b mod 8)*chunk + (i mod chunk) with i = b div 8.
+ */
+int varlen_launch_shape(int32_t max_q, int32_t num_reqs, int32_t H, int32_t D, int dtype_f32,
+                        int32_t* block_m, int32_t* chunk, int64_t* blocks);
+int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, int32_t max_q,
+                    int32_t num_reqs, int32_t H, int32_t D, int dtype_f32, int32_t* triples_out,
+                    int64_t max_blocks, vl_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARLEN_MI355X_H */

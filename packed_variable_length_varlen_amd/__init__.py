@@ -1,0 +1,304 @@
+"""Packed variable-length attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/varlen.h.  Every function here
+only checks and marshals arguments (torch tensors -> device pointers, the
+current HIP stream) and calls the shared library; all computation runs in the
+library's HIP kernels.  There is no fallback: if the library is not built, or
+the tensors are not on the GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "load_library", "lib_path", "cu_seqlens_from_lengths", "joint_cu_seqlens",
+    "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "varlen_attn_fwd", "varlen_attn_fwd_f32",
+    "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
+    "VarlenError",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libvarlen_mi355x.so"
+_lib = None
+
+_c_int = ctypes.c_int
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_f32 = ctypes.c_float
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "vl_version": ([], _c_int),
+    "vl_status_string": ([_c_int], ctypes.c_char_p),
+    "cu_seqlens_from_lengths": ([_vp, _c_i32, _vp, _vp], _c_int),
+    "joint_cu_seqlens": ([_vp, _c_i32, _vp, _c_i32, _vp, _vp, _vp, _vp, _vp], _c_int),
+    "pack_by_cu_seqlens": ([_vp, _c_i64, _vp, _c_i32, _c_i64, _vp, _vp, _vp], _c_int),
+    "unpack_by_cu_seqlens": ([_vp, _vp, _vp, _c_i32, _c_i64, _vp, _c_i64, _c_int, _vp], _c_int),
+    "varlen_attn_fwd": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                         _vp, _vp, _vp], _c_int),
+    "varlen_attn_fwd_f32": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                             _c_f32, _vp, _vp, _vp], _c_int),
+    "block_local_attn_fwd": ([_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                              _c_i32, _c_f32, _vp, _vp, _vp], _c_int),
+    "block_local_attn_fwd_f32": ([_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                  _c_i32, _c_f32, _vp, _vp, _vp], _c_int),
+    "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_int, _vp, _vp, _vp], _c_int),
+    "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _vp, _c_i64, _vp],
+                        _c_int),
+}
+
+
+class VarlenError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise VarlenError(
+            f"{_LIB_NAME} is not built; run `python -m packed_variable_length_varlen_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().vl_status_string(rc).decode()
+        raise VarlenError(f"{what} failed: {msg} ({rc})")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _gpu(t: torch.Tensor, name: str, dtype=None, contiguous: bool = True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise VarlenError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise VarlenError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ boundaries
+
+
+def cu_seqlens_from_lengths(lengths: torch.Tensor, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    _gpu(lengths, "lengths", torch.int32)
+    R = lengths.numel()
+    if out is None:
+        out = torch.empty(R + 1, dtype=torch.int32, device=lengths.device)
+    _gpu(out, "out", torch.int32)
+    _check(load_library().cu_seqlens_from_lengths(_ptr(lengths), R, _ptr(out), _stream(stream)),
+           "cu_seqlens_from_lengths")
+    return out
+
+
+def joint_cu_seqlens(text_mask: torch.Tensor, img_hw: torch.Tensor, outs=None, stream=None):
+    """Returns (cu_joint, cu_text, cu_img, img_dst), all int32 on the GPU."""
+    _gpu(text_mask, "text_mask", torch.uint8)
+    _gpu(img_hw, "img_hw", torch.int32)
+    R, cap = text_mask.shape
+    if tuple(img_hw.shape) != (R, 2):
+        raise VarlenError("img_hw must be [num_reqs, 2]")
+    dev = text_mask.device
+    if outs is None:
+        outs = (torch.empty(R + 1, dtype=torch.int32, device=dev),
+                torch.empty(R + 1, dtype=torch.int32, device=dev),
+                torch.empty(R + 1, dtype=torch.int32, device=dev),
+                torch.empty(R, dtype=torch.int32, device=dev))
+    for i, t in enumerate(outs):
+        _gpu(t, f"outs[{i}]", torch.int32)
+    _check(load_library().joint_cu_seqlens(_ptr(text_mask), cap, _ptr(img_hw), R, *[_ptr(t) for t in outs],
+                                           _stream(stream)), "joint_cu_seqlens")
+    return outs
+
+
+# ------------------------------------------------------------------ pack / unpack
+
+
+def pack_by_cu_seqlens(src_padded: torch.Tensor, cu_seqlens: torch.Tensor, dst_flat: torch.Tensor,
+                       dst_row_offsets: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """src_padded [R, max_len, ...] -> rows of dst_flat [T, ...] (same row shape)."""
+    _gpu(src_padded, "src_padded")
+    _gpu(dst_flat, "dst_flat", src_padded.dtype)
+    _gpu(cu_seqlens, "cu_seqlens", torch.int32)
+    if dst_row_offsets is not None:
+        _gpu(dst_row_offsets, "dst_row_offsets", torch.int32)
+    R = cu_seqlens.numel() - 1
+    if src_padded.shape[0] != R or tuple(src_padded.shape[2:]) != tuple(dst_flat.shape[1:]):
+        raise VarlenError("src_padded must be [num_reqs, max_len, *row] and dst_flat [T, *row]")
+    row_bytes = dst_flat[0].numel() * dst_flat.element_size() if dst_flat.dim() > 1 else dst_flat.element_size()
+    _check(load_library().pack_by_cu_seqlens(_ptr(src_padded), src_padded.shape[1], _ptr(cu_seqlens), R,
+                                             row_bytes, _ptr(dst_flat), _ptr(dst_row_offsets),
+                                             _stream(stream)), "pack_by_cu_seqlens")
+    return dst_flat
+
+
+def unpack_by_cu_seqlens(src_flat: torch.Tensor, cu_seqlens: torch.Tensor, dst_padded: torch.Tensor,
+                         src_row_offsets: Optional[torch.Tensor] = None, zero_fill: bool = True,
+                         stream=None) -> torch.Tensor:
+    """Rows of src_flat [T, ...] -> dst_padded [R, max_len, ...]."""
+    _gpu(src_flat, "src_flat")
+    _gpu(dst_padded, "dst_padded", src_flat.dtype)
+    _gpu(cu_seqlens, "cu_seqlens", torch.int32)
+    if src_row_offsets is not None:
+        _gpu(src_row_offsets, "src_row_offsets", torch.int32)
+    R = cu_seqlens.numel() - 1
+    if dst_padded.shape[0] != R or tuple(dst_padded.shape[2:]) != tuple(src_flat.shape[1:]):
+        raise VarlenError("dst_padded must be [num_reqs, max_len, *row] and src_flat [T, *row]")
+    row_bytes = src_flat[0].numel() * src_flat.element_size() if src_flat.dim() > 1 else src_flat.element_size()
+    _check(load_library().unpack_by_cu_seqlens(_ptr(src_flat), _ptr(src_row_offsets), _ptr(cu_seqlens), R,
+                                               row_bytes, _ptr(dst_padded), dst_padded.shape[1],
+                                               1 if zero_fill else 0, _stream(stream)),
+           "unpack_by_cu_seqlens")
+    return dst_padded
+
+
+# ------------------------------------------------------------------ attention
+
+
+def _attn_prep(q, k, v, dtype):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _gpu(t, name, dtype)
+    if q.dim() != k.dim() or k.shape != v.shape or q.shape[-2:] != k.shape[-2:]:
+        raise VarlenError("q, k, v must agree on heads and head_dim, and k, v on shape")
+
+
+def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse, padded_tokens,
+            attn_mask, return_lse, stream):
+    # The flat path rejects attention masks and needs padded_tokens == 0
+    # (vLLM-Omni PR #6711, "Reference / Acknowledgement").
+    if attn_mask is not None:
+        raise VarlenError("the flat varlen path takes no attention mask")
+    if padded_tokens != 0:
+        raise VarlenError("the flat varlen path requires padded_tokens == 0")
+    _attn_prep(q, k, v, dtype)
+    if q.dim() != 3:
+        raise VarlenError("q, k, v must be packed [total_tokens, heads, head_dim]")
+    _gpu(q_cu, "q_cu_seqlens", torch.int32)
+    _gpu(kv_cu, "kv_cu_seqlens", torch.int32)
+    R = q_cu.numel() - 1
+    if kv_cu.numel() != R + 1:
+        raise VarlenError("q_cu_seqlens and kv_cu_seqlens disagree on the number of requests")
+    T, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _gpu(out, "out", dtype)
+    if out.shape != q.shape:
+        raise VarlenError("out must have the shape of q")
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (T, H):
+            raise VarlenError("lse must be [total_tokens, heads]")
+    rc = getattr(load_library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(q_cu), _ptr(kv_cu), int(max_q),
+                                          int(max_kv), R, H, D, float(scale), _ptr(out), _ptr(lse),
+                                          _stream(stream))
+    _check(rc, fn_name)
+    return (out, lse) if return_lse else out
+
+
+def varlen_attn_fwd(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
+                    lse=None, padded_tokens: int = 0, attn_mask=None, return_lse: bool = False,
+                    stream=None):
+    """bf16 packed [T, H, D] varlen attention; returns out (and lse if asked)."""
+    return _varlen("varlen_attn_fwd", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream)
+
+
+def varlen_attn_fwd_f32(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
+                        lse=None, padded_tokens: int = 0, attn_mask=None, return_lse: bool = False,
+                        stream=None):
+    """float32 packed [T, H, D] varlen attention; returns out (and lse if asked)."""
+    return _varlen("varlen_attn_fwd_f32", torch.float32, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream)
+
+
+def _block_local(fn_name, dtype, q, k, v, block, look_back, look_ahead, scale, out, lse, return_lse,
+                 stream):
+    _attn_prep(q, k, v, dtype)
+    if q.dim() != 4 or q.shape != k.shape:
+        raise VarlenError("q, k, v must be [batch, frames, heads, head_dim] of one shape")
+    B, n, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _gpu(out, "out", dtype)
+    if lse is None and return_lse:
+        lse = torch.empty((B, n, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _gpu(lse, "lse", torch.float32)
+    rc = getattr(load_library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), B, n, H, D, int(block), int(look_back),
+                                          int(look_ahead), float(scale), _ptr(out), _ptr(lse),
+                                          _stream(stream))
+    _check(rc, fn_name)
+    return (out, lse) if return_lse else out
+
+
+def block_local_attn_fwd(q, k, v, block: int, look_back: int, look_ahead: int, scale=None, out=None,
+                         lse=None, return_lse: bool = False, stream=None):
+    """bf16 block-local attention over [B, n, H, D]."""
+    return _block_local("block_local_attn_fwd", torch.bfloat16, q, k, v, block, look_back, look_ahead,
+                        scale, out, lse, return_lse, stream)
+
+
+def block_local_attn_fwd_f32(q, k, v, block: int, look_back: int, look_ahead: int, scale=None, out=None,
+                             lse=None, return_lse: bool = False, stream=None):
+    """float32 block-local attention over [B, n, H, D]."""
+    return _block_local("block_local_attn_fwd_f32", torch.float32, q, k, v, block, look_back, look_ahead,
+                        scale, out, lse, return_lse, stream)
+
+
+# ------------------------------------------------------------------ schedule export
+
+
+def varlen_launch_shape(max_q: int, num_reqs: int, H: int, D: int, f32: bool = False) -> Tuple[int, int, int]:
+    bm, ch, nb = _c_i32(), _c_i32(), _c_i64()
+    _check(load_library().varlen_launch_shape(max_q, num_reqs, H, D, 1 if f32 else 0, ctypes.byref(bm),
+                                              ctypes.byref(ch), ctypes.byref(nb)), "varlen_launch_shape")
+    return bm.value, ch.value, nb.value
+
+
+def varlen_tile_map(q_cu: torch.Tensor, kv_cu: torch.Tensor, max_q: int, H: int, D: int, f32: bool = False,
+                    stream=None) -> torch.Tensor:
+    """[blocks, 3] int32 (request, head, q-tile) per launched work-group, -1 if idle."""
+    _gpu(q_cu, "q_cu", torch.int32)
+    _gpu(kv_cu, "kv_cu", torch.int32)
+    R = q_cu.numel() - 1
+    _, _, G = varlen_launch_shape(max_q, R, H, D, f32)
+    out = torch.empty((max(G, 1), 3), dtype=torch.int32, device=q_cu.device)
+    _check(load_library().varlen_tile_map(_ptr(q_cu), _ptr(kv_cu), int(max_q), R, H, D, 1 if f32 else 0,
+                                          _ptr(out), max(G, 1), _stream(stream)), "varlen_tile_map")
+    return out[:G]

@@ -1,0 +1,237 @@
+// Boundaries (cu_seqlens) and pack / unpack gathers for gfx950.
+//
+// pack: only real tokens of each request enter the flat buffer (vLLM-Omni
+// PR #4024 "How batching works"); unpack scatters flat rows back to the
+// per-request padded layout (PR #6711 "Key changes": output unpacked by
+// cu_seqlens).  A request's rows are contiguous on both sides, so each request
+// is one contiguous copy of len_r * row_bytes bytes: the kernels stream it
+// with the widest aligned vector, several independent loads in flight per
+// thread, and no per-row index arithmetic.
+#include "vl_device.h"
+
+namespace vl {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+constexpr int kUnitsPerBlock = kCopyThreads * kCopyUnroll;
+
+// Request r = blockIdx.y copies units [0, len_r*row_units) of its slab in
+// src (starting at r * src_slab_units) to dst starting at off_r * row_units;
+// with zero_tail, units [len_r*row_units, slab_units) of the destination slab
+// are zeroed (unpack).  For pack, the destination is flat (dst_flat = true).
+template <typename U, bool kPack>
+__global__ void __launch_bounds__(kCopyThreads) copy_segments_kernel(
+    const U* __restrict__ src, U* __restrict__ dst, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ offsets, int64_t row_units, int64_t slab_rows, int zero_tail) {
+  const int r = blockIdx.y;
+  const int64_t len = (int64_t)(cu[r + 1] - cu[r]);
+  const int64_t off = offsets != nullptr ? (int64_t)offsets[r] : (int64_t)cu[r];
+  const int64_t real_units = len * row_units;
+  const int64_t span_units = (!kPack && zero_tail) ? slab_rows * row_units : real_units;
+  const int64_t u0 = (int64_t)blockIdx.x * kUnitsPerBlock;
+  if (u0 >= span_units) return;
+  const U* s;
+  U* d;
+  if (kPack) {
+    s = src + (int64_t)r * slab_rows * row_units;
+    d = dst + off * row_units;
+  } else {
+    s = src + off * row_units;
+    d = dst + (int64_t)r * slab_rows * row_units;
+  }
+  U buf[kCopyUnroll];
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
+    buf[i] = u < real_units ? s[u] : U{};
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
+    if (u < span_units) d[u] = buf[i];
+  }
+}
+
+// Inclusive scan of one value per thread over a 256-thread block.
+__device__ __forceinline__ int block_scan_256(int x, int* lds8) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) lds8[wave] = incl;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += lds8[w];
+  __syncthreads();
+  return incl + add;
+}
+
+// One 256-thread block: cu_out[0] = 0, cu_out[r+1] = sum of lengths[0..r].
+__global__ void __launch_bounds__(256) cu_from_lengths_kernel(const int32_t* __restrict__ lengths,
+                                                              int R, int32_t* __restrict__ cu) {
+  __shared__ int lds8[8];
+  __shared__ int carry_s;
+  if (threadIdx.x == 0) {
+    cu[0] = 0;
+    carry_s = 0;
+  }
+  __syncthreads();
+  for (int r0 = 0; r0 < R; r0 += 256) {
+    const int r = r0 + threadIdx.x;
+    const int x = r < R ? lengths[r] : 0;
+    const int incl = block_scan_256(x, lds8);
+    const int carry = carry_s;
+    if (r < R) cu[r + 1] = carry + incl;
+    __syncthreads();
+    if (threadIdx.x == 255) carry_s = carry + incl;
+    __syncthreads();
+  }
+}
+
+// One 256-thread block: text lengths from the mask, image tokens from the
+// grids, and the joint / text / image boundaries plus each image segment's
+// first packed row.
+__global__ void __launch_bounds__(256) joint_cu_kernel(const uint8_t* __restrict__ mask,
+                                                       int text_cap, const int32_t* __restrict__ hw,
+                                                       int R, int32_t* cu_joint, int32_t* cu_text,
+                                                       int32_t* cu_img, int32_t* img_dst) {
+  __shared__ int lds8[8];
+  __shared__ int carry[3];
+  if (threadIdx.x < 3) carry[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    if (cu_joint) cu_joint[0] = 0;
+    if (cu_text) cu_text[0] = 0;
+    if (cu_img) cu_img[0] = 0;
+  }
+  __syncthreads();
+  for (int r0 = 0; r0 < R; r0 += 256) {
+    const int r = r0 + threadIdx.x;
+    int t = 0, n = 0;
+    if (r < R) {
+      const uint8_t* m = mask + (int64_t)r * text_cap;
+      for (int j = 0; j < text_cap; ++j) t += m[j] != 0;
+      n = hw[2 * r] * hw[2 * r + 1];
+    }
+    const int it = block_scan_256(t, lds8);
+    const int in = block_scan_256(n, lds8);
+    const int ij = block_scan_256(t + n, lds8);
+    const int ct = carry[0], cn = carry[1], cj = carry[2];
+    if (r < R) {
+      if (cu_text) cu_text[r + 1] = ct + it;
+      if (cu_img) cu_img[r + 1] = cn + in;
+      if (cu_joint) cu_joint[r + 1] = cj + ij;
+      if (img_dst) img_dst[r] = cj + ij - (t + n) + t;
+    }
+    __syncthreads();
+    if (threadIdx.x == 255) {
+      carry[0] = ct + it;
+      carry[1] = cn + in;
+      carry[2] = cj + ij;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace vl
+
+// ============================================================================ host side
+
+namespace {
+
+constexpr int kMaxReqs = 65535;  // grid.y bound of the copy kernels
+
+int launch_status() { return hipGetLastError() == hipSuccess ? VL_OK : VL_ELAUNCH; }
+
+template <bool kPack>
+int copy_common(const void* src, void* dst, const int32_t* cu, const int32_t* offsets,
+                int32_t num_reqs, int64_t row_bytes, int64_t slab_rows, int zero_tail,
+                hipStream_t stream) {
+  if (num_reqs < 0 || num_reqs > kMaxReqs || row_bytes <= 0 || slab_rows < 0) return VL_EINVAL;
+  if (num_reqs == 0 || slab_rows == 0) return VL_OK;
+  if (!src || !dst || !cu) return VL_EINVAL;
+  const uintptr_t a = (uintptr_t)src | (uintptr_t)dst;
+  int64_t unit;
+  if (row_bytes % 16 == 0 && (a & 15u) == 0)
+    unit = 16;
+  else if (row_bytes % 4 == 0 && (a & 3u) == 0)
+    unit = 4;
+  else
+    unit = 1;
+  const int64_t row_units = row_bytes / unit;
+  const int64_t slab_units = slab_rows * row_units;
+  const int64_t bx = (slab_units + vl::kUnitsPerBlock - 1) / vl::kUnitsPerBlock;
+  if (bx > INT32_MAX) return VL_EUNSUPPORTED;
+  const dim3 grid((unsigned)bx, (unsigned)num_reqs);
+  (void)hipGetLastError();
+  if (unit == 16)
+    hipLaunchKernelGGL((vl::copy_segments_kernel<vl::u32x4, kPack>), grid, dim3(vl::kCopyThreads), 0,
+                       stream, (const vl::u32x4*)src, (vl::u32x4*)dst, cu, offsets, row_units,
+                       slab_rows, zero_tail);
+  else if (unit == 4)
+    hipLaunchKernelGGL((vl::copy_segments_kernel<uint32_t, kPack>), grid, dim3(vl::kCopyThreads), 0,
+                       stream, (const uint32_t*)src, (uint32_t*)dst, cu, offsets, row_units,
+                       slab_rows, zero_tail);
+  else
+    hipLaunchKernelGGL((vl::copy_segments_kernel<uint8_t, kPack>), grid, dim3(vl::kCopyThreads), 0,
+                       stream, (const uint8_t*)src, (uint8_t*)dst, cu, offsets, row_units,
+                       slab_rows, zero_tail);
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int vl_version(void) { return 100; }
+
+const char* vl_status_string(int status) {
+  switch (status) {
+    case VL_OK: return "ok";
+    case VL_EINVAL: return "invalid argument";
+    case VL_EUNSUPPORTED: return "unsupported size";
+    case VL_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int cu_seqlens_from_lengths(const int32_t* lengths, int32_t num_reqs, int32_t* cu_out,
+                            vl_stream_t stream) {
+  if (num_reqs < 0 || num_reqs > kMaxReqs + 1 || !cu_out) return VL_EINVAL;
+  if (num_reqs > 0 && !lengths) return VL_EINVAL;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(vl::cu_from_lengths_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream,
+                     lengths, num_reqs, cu_out);
+  return launch_status();
+}
+
+int joint_cu_seqlens(const uint8_t* text_mask, int32_t text_cap, const int32_t* img_hw,
+                     int32_t num_reqs, int32_t* cu_joint, int32_t* cu_text, int32_t* cu_img,
+                     int32_t* img_dst, vl_stream_t stream) {
+  if (num_reqs < 0 || num_reqs > kMaxReqs + 1 || text_cap < 0) return VL_EINVAL;
+  if (num_reqs > 0 && (!img_hw || (text_cap > 0 && !text_mask))) return VL_EINVAL;
+  if (!cu_joint && !cu_text && !cu_img && !img_dst) return VL_OK;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(vl::joint_cu_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, text_mask,
+                     text_cap, img_hw, num_reqs, cu_joint, cu_text, cu_img, img_dst);
+  return launch_status();
+}
+
+int pack_by_cu_seqlens(const void* src_padded, int64_t max_len, const int32_t* cu_seqlens,
+                       int32_t num_reqs, int64_t row_bytes, void* dst_flat,
+                       const int32_t* dst_row_offsets, vl_stream_t stream) {
+  return copy_common<true>(src_padded, dst_flat, cu_seqlens, dst_row_offsets, num_reqs, row_bytes,
+                           max_len, 0, (hipStream_t)stream);
+}
+
+int unpack_by_cu_seqlens(const void* src_flat, const int32_t* src_row_offsets,
+                         const int32_t* cu_seqlens, int32_t num_reqs, int64_t row_bytes,
+                         void* dst_padded, int64_t max_len, int zero_fill, vl_stream_t stream) {
+  return copy_common<false>(src_flat, dst_padded, cu_seqlens, src_row_offsets, num_reqs, row_bytes,
+                            max_len, zero_fill, (hipStream_t)stream);
+}
+
+}  // extern "C"

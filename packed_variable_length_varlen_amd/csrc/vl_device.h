@@ -1,0 +1,135 @@
+// Device-side helpers shared by the kernels of the library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/varlen.h"
+
+namespace vl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kXcds = 8;          // chiplets; block ids are dealt to them round-robin
+constexpr int kLptMaxReqs = 64;   // longest-first request order up to this many requests
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int readlane(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// Value of x in lane (l xor 32), through the gfx950 lane-half swap (one VALU op).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return lane_id() < 32 ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
+}
+
+// x[lane] combined with x[lane xor 32]; symmetric in the two halves.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Launched block id -> logical tile: the i-th block chiplet x (= b mod 8)
+// receives takes tile ((i div chunk) * 8 + x) * chunk + (i mod chunk).
+__device__ __forceinline__ int block_to_logical(int b, int chunk) {
+  const int x = b % kXcds;
+  const int i = b / kXcds;
+  return ((i / chunk) * kXcds + x) * chunk + (i % chunk);
+}
+
+// Logical tile t -> (request, head, q-tile) of the varlen schedule; req = -1
+// when t is past the last tile.  Requests are visited by key length
+// descending (ties: lower index first) when R <= kLptMaxReqs, else in index
+// order; inside a request heads ascend, then q-tiles.  Executed by a whole
+// wave (all 64 lanes active); the result is wave-uniform.
+__device__ __forceinline__ void find_tile(const int32_t* __restrict__ q_cu,
+                                          const int32_t* __restrict__ kv_cu, int R, int H,
+                                          int block_m, int t, int& req, int& head, int& qtile) {
+  const int lane = lane_id();
+  req = -1;
+  head = 0;
+  qtile = 0;
+  if (R <= kLptMaxReqs) {
+    int kvlen = -1, nt = 0, cnt = 0;
+    if (lane < R) {
+      const int qlen = q_cu[lane + 1] - q_cu[lane];
+      kvlen = kv_cu[lane + 1] - kv_cu[lane];
+      nt = (qlen + block_m - 1) / block_m;
+      cnt = nt * H;
+    }
+    int rank = 0;
+    for (int s = 0; s < R; ++s) {
+      const int kv_s = readlane(kvlen, s);
+      rank += (kv_s > kvlen) || (kv_s == kvlen && s < lane);
+    }
+    int start = 0;
+    for (int s = 0; s < R; ++s) {
+      const int rank_s = readlane(rank, s);
+      const int cnt_s = readlane(cnt, s);
+      start += (rank_s < rank) ? cnt_s : 0;
+    }
+    const bool hit = lane < R && cnt > 0 && t >= start && t < start + cnt;
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      const int r = __ffsll((unsigned long long)m) - 1;
+      const int st = readlane(start, r);
+      const int ntr = readlane(nt, r);
+      const int local = t - st;
+      req = r;
+      head = local / ntr;
+      qtile = local % ntr;
+    }
+  } else {
+    int base = 0;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int r = r0 + lane;
+      int nt = 0, cnt = 0;
+      if (r < R) {
+        nt = (q_cu[r + 1] - q_cu[r] + block_m - 1) / block_m;
+        cnt = nt * H;
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const int excl = incl - cnt;
+      const bool hit = cnt > 0 && t >= base + excl && t < base + incl;
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        const int l = __ffsll((unsigned long long)m) - 1;
+        const int st = base + readlane(excl, l);
+        const int ntr = readlane(nt, l);
+        const int local = t - st;
+        req = r0 + l;
+        head = local / ntr;
+        qtile = local % ntr;
+        return;
+      }
+      base += readlane(incl, 63);
+      if (t < base) return;
+    }
+  }
+}
+
+// Host-side launch size: upper bound on the tile count, rounded up to whole
+// groups of (chiplets x chunk) so the block -> tile map is a bijection.
+inline int64_t grid_blocks(int64_t num_reqs, int64_t max_q, int64_t H, int64_t block_m,
+                           int64_t chunk) {
+  const int64_t upper = num_reqs * H * ((max_q + block_m - 1) / block_m);
+  const int64_t group = kXcds * chunk;
+  return ((upper + group - 1) / group) * group;
+}
+
+}  // namespace vl

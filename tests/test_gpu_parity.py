@@ -1,0 +1,397 @@
+"""GPU path vs the CPU oracle, through the C ABI (via the Python binding).
+
+Integer work (boundaries, pack/unpack, the tile schedule) must be bit-exact.
+Attention must be within the stated tolerances of the fp64 oracle: bf16
+max-abs 2e-2 and mean-abs 2e-3, fp32 max-abs 1e-5.  Output buffers are
+surrounded by canary rows that must survive every call.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import packed_variable_length_varlen_amd as vl
+from packed_variable_length_varlen_amd import workloads as wl
+from tests.helpers import check_close, check_lse, sample_rows, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def canary_out(shape, dtype, pad=3):
+    """An output view with `pad` NaN-filled canary rows on either side."""
+    full = torch.full((shape[0] + 2 * pad,) + tuple(shape[1:]), float("nan"), dtype=dtype, device=DEV)
+    return full, full[pad:pad + shape[0]]
+
+
+def assert_canary(full, pad=3):
+    head = full[:pad].float()
+    tail = full[full.shape[0] - pad:].float()
+    assert torch.isnan(head).all() and torch.isnan(tail).all(), "a kernel wrote outside its output"
+
+
+# ------------------------------------------------------------------ boundaries
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_joint_cu_seqlens_bitexact(cfg):
+    log(f"[joint_cu] config {cfg}")
+    spec = wl.CONFIGS[cfg]
+    rng = np.random.default_rng(cfg)
+    R = len(spec.img_grids)
+    mask = np.zeros((R, wl.TEXT_CAP), dtype=bool)
+    for r, (lo, hi) in enumerate(spec.text_ranges):
+        mask[r, :int(rng.integers(lo, hi + 1))] = True
+    hw = np.array(spec.img_grids, dtype=np.int32).reshape(R, 2)
+    outs = vl.joint_cu_seqlens(torch.from_numpy(mask.astype(np.uint8)).to(DEV), torch.from_numpy(hw).to(DEV))
+    ref = oracle.joint_cu_seqlens(mask, hw)
+    for got, exp in zip(outs, ref):
+        assert np.array_equal(got.cpu().numpy(), exp.astype(np.int32))
+
+
+@pytest.mark.parametrize("R", [0, 1, 5, 255, 256, 257, 1000, 3000])
+def test_cu_seqlens_and_joint_random_bitexact(R):
+    log(f"[cu] R={R}")
+    rng = np.random.default_rng(R)
+    lengths = rng.integers(0, 5000, size=R).astype(np.int32)
+    cu = vl.cu_seqlens_from_lengths(torch.from_numpy(lengths).to(DEV))
+    assert np.array_equal(cu.cpu().numpy(), oracle.cu_seqlens_from_lengths(lengths).astype(np.int32))
+    # scattered (non-prefix) masks and empty grids
+    mask = rng.random((R, 77)) < 0.3
+    hw = rng.integers(0, 40, size=(R, 2)).astype(np.int32)
+    outs = vl.joint_cu_seqlens(torch.from_numpy(mask.astype(np.uint8)).to(DEV), torch.from_numpy(hw).to(DEV))
+    for got, exp in zip(outs, oracle.joint_cu_seqlens(mask, hw)):
+        assert np.array_equal(got.cpu().numpy(), exp.astype(np.int32))
+
+
+# ------------------------------------------------------------------ pack / unpack
+
+
+@pytest.mark.parametrize("row_shape,dtype", [((24, 128), torch.bfloat16), ((3,), torch.float32),
+                                             ((3,), torch.bfloat16), ((5,), torch.uint8),
+                                             ((2, 64), torch.float32)])
+def test_pack_unpack_bitexact_vector_widths(row_shape, dtype):
+    log(f"[pack] row {row_shape} {dtype}")
+    lengths = [0, 17, 1, 300, 0, 129, 64]
+    S = 320
+    rng = np.random.default_rng(7)
+    src = torch.from_numpy(rng.standard_normal((len(lengths), S) + row_shape).astype(np.float32)).to(dtype)
+    cu = oracle.cu_seqlens_from_lengths(lengths)
+    T = int(cu[-1])
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+    full, dst = canary_out((T,) + row_shape, dtype) if dtype != torch.uint8 else (None, torch.empty((T,) + row_shape, dtype=dtype, device=DEV))
+    vl.pack_by_cu_seqlens(src.to(DEV), cu_d, dst)
+    ref = oracle.pack_by_cu_seqlens(src.numpy() if dtype != torch.bfloat16 else src.view(torch.int16).numpy(), cu)
+    got = dst.cpu().numpy() if dtype != torch.bfloat16 else dst.cpu().view(torch.int16).numpy()
+    assert np.array_equal(got, ref)
+    if full is not None:
+        assert_canary(full)
+    # unpack back, with and without zero fill
+    for zero_fill in (True, False):
+        back = torch.full((len(lengths), S) + row_shape, 7, dtype=dtype, device=DEV)
+        vl.unpack_by_cu_seqlens(dst, cu_d, back, zero_fill=zero_fill)
+        init = np.full((len(lengths), S) + row_shape, 7, dtype=ref.dtype)
+        if dtype == torch.bfloat16:
+            init = torch.full((1,), 7, dtype=dtype).view(torch.int16).numpy()[0] * np.ones_like(init)
+        exp = oracle.unpack_by_cu_seqlens(ref, cu, S, zero_fill=zero_fill, dst=init)
+        gotb = back.cpu().numpy() if dtype != torch.bfloat16 else back.cpu().view(torch.int16).numpy()
+        assert np.array_equal(gotb, exp)
+
+
+def test_joint_pack_with_offsets_bitexact():
+    log("[pack] joint text+image with offsets")
+    inp = wl.make_varlen_inputs(wl.CONFIGS[3], torch.bfloat16)
+    mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
+    hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV)
+    cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
+    T = inp.total_tokens
+    H, D = inp.spec.H, inp.spec.D
+    full, q = canary_out((T, H, D), torch.bfloat16)
+    vl.pack_by_cu_seqlens(inp.q_text.to(DEV), cu_t, q, dst_row_offsets=cu_j[:-1])
+    vl.pack_by_cu_seqlens(inp.q_img.to(DEV), cu_i, q, dst_row_offsets=img_dst)
+    assert_canary(full)
+    cj, ct, ci, idst = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
+    ref = np.zeros((T, H, D), dtype=np.int16)
+    oracle.pack_by_cu_seqlens(inp.q_text.view(torch.int16).numpy(), ct, dst_row_offsets=cj[:-1], dst=ref)
+    oracle.pack_by_cu_seqlens(inp.q_img.view(torch.int16).numpy(), ci, dst_row_offsets=idst, dst=ref)
+    assert np.array_equal(q.cpu().view(torch.int16).numpy(), ref)
+
+
+# ------------------------------------------------------------------ tile schedule
+
+
+@pytest.mark.parametrize("case", ["lpt", "ties", "index_order", "empty", "qkv_differ"])
+def test_tile_map_bitexact(case):
+    log(f"[tile_map] {case}")
+    rng = np.random.default_rng(3)
+    if case == "lpt":
+        ql = [17, 64, 129, 4096, 300, 1]
+        kl = ql
+    elif case == "ties":
+        ql = [128] * 5 + [256, 256]
+        kl = ql
+    elif case == "index_order":
+        ql = list(rng.integers(0, 700, size=150))
+        kl = ql
+    elif case == "empty":
+        ql = [0, 0, 5, 0]
+        kl = [0, 3, 5, 0]
+    else:
+        ql = [100, 1, 200, 33]
+        kl = [5, 400, 1, 33]
+    H, D = 3, 128
+    q_cu = oracle.cu_seqlens_from_lengths(ql)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    max_q = max(max(ql), 1)
+    bm, chunk, G = vl.varlen_launch_shape(max_q, len(ql), H, D)
+    got = vl.varlen_tile_map(torch.from_numpy(q_cu.astype(np.int32)).to(DEV),
+                             torch.from_numpy(kv_cu.astype(np.int32)).to(DEV), max_q, H, D).cpu().numpy()
+    ref = oracle.block_schedule(q_cu, kv_cu, H, bm, max_q, chunk)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref.astype(np.int32))
+
+
+# ------------------------------------------------------------------ varlen attention
+
+
+def _run_varlen(q, k, v, q_cu, kv_cu, scale, f32, max_q=None, max_kv=None):
+    ql = np.diff(q_cu)
+    kl = np.diff(kv_cu)
+    max_q = int(ql.max()) if max_q is None and ql.size else (max_q or 0)
+    max_kv = int(kl.max()) if max_kv is None and kl.size else (max_kv or 0)
+    dtype = torch.float32 if f32 else torch.bfloat16
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    full, out = canary_out(tuple(q.shape), dtype)
+    lse_full, lse = canary_out((q.shape[0], q.shape[1]), torch.float32)
+    fn = vl.varlen_attn_fwd_f32 if f32 else vl.varlen_attn_fwd
+    fn(qd, kd, vd, torch.from_numpy(np.asarray(q_cu, dtype=np.int32)).to(DEV),
+       torch.from_numpy(np.asarray(kv_cu, dtype=np.int32)).to(DEV), max_q, max_kv, scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert_canary(full)
+    assert_canary(lse_full)
+    return out, lse
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_varlen_tiny_config_full(f32):
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[varlen] config 1 {dtype}")
+    inp = wl.make_varlen_inputs(wl.CONFIGS[1], dtype)
+    cu, cu_t, _, _ = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
+    q = torch.from_numpy(oracle.pack_by_cu_seqlens(inp.q_text.float().numpy(), cu_t)).to(dtype)
+    k = torch.from_numpy(oracle.pack_by_cu_seqlens(inp.k_text.float().numpy(), cu_t)).to(dtype)
+    v = torch.from_numpy(oracle.pack_by_cu_seqlens(inp.v_text.float().numpy(), cu_t)).to(dtype)
+    out, lse = _run_varlen(q, k, v, cu, cu, inp.scale, f32)
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), cu, cu, inp.scale)
+    mx, mean = check_close(to64(out), ro, f32, "config 1")
+    check_lse(to64(lse), rl, f32, "config 1")
+    log(f"   max-abs {mx:.3g} mean-abs {mean:.3g}")
+
+
+EDGE_CASES = [
+    ("ragged", [1, 31, 32, 33, 127, 128, 129, 200], None, 2),
+    ("empty_and_zero_kv", [0, 5, 40, 0, 3], [0, 0, 40, 7, 3], 3),
+    ("q_ne_kv", [7, 140, 20], [300, 9, 129], 2),
+    ("single_key", [65], [1], 1),
+    ("many_requests_index_order", [int(x) for x in np.random.default_rng(5).integers(0, 90, size=100)], None, 1),
+]
+
+
+@pytest.mark.parametrize("name,ql,kl,H", EDGE_CASES)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("f32", [False, True])
+def test_varlen_edge_cases(name, ql, kl, H, D, f32):
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[varlen] {name} D={D} {dtype}")
+    kl = ql if kl is None else kl
+    q, k, v = wl.random_varlen_case(17, ql, H, D, dtype, kl)
+    q_cu = oracle.cu_seqlens_from_lengths(ql)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    scale = wl.softmax_scale(D)
+    out, lse = _run_varlen(q, k, v, q_cu, kv_cu, scale, f32)
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), q_cu, kv_cu, scale)
+    check_close(to64(out), ro, f32, name)
+    check_lse(to64(lse), rl, f32, name)
+
+
+def test_varlen_loose_max_bounds_and_large_values():
+    """max_q/max_kv only size the launch: larger bounds give the same bits;
+    scaled inputs (|s| up to ~60) stay finite and within tolerance."""
+    log("[varlen] loose bounds / large scores")
+    ql = [100, 300, 7]
+    q, k, v = wl.random_varlen_case(23, ql, 2, 128, torch.bfloat16)
+    cu = oracle.cu_seqlens_from_lengths(ql)
+    o1, l1 = _run_varlen(q, k, v, cu, cu, 0.088388, False)
+    o2, l2 = _run_varlen(q, k, v, cu, cu, 0.088388, False, max_q=1000, max_kv=5000)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    q4 = (q.float() * 4).to(torch.bfloat16)
+    o3, l3 = _run_varlen(q4, k, v, cu, cu, 0.088388, False)
+    ro, rl = oracle.varlen_attention(to64(q4), to64(k), to64(v), cu, cu, 0.088388)
+    check_close(to64(o3), ro, False, "scaled q")
+
+
+def test_varlen_invariants_bitwise():
+    """Alone == inside the packed batch, permutation permutes outputs, and two
+    runs give the same bits (the tiles never mix requests)."""
+    log("[varlen] invariants")
+    ql = [300, 77, 1000, 129]
+    H, D = 3, 128
+    q, k, v = wl.random_varlen_case(31, ql, H, D, torch.bfloat16)
+    cu = oracle.cu_seqlens_from_lengths(ql)
+    out, lse = _run_varlen(q, k, v, cu, cu, 0.1, False)
+    out2, lse2 = _run_varlen(q, k, v, cu, cu, 0.1, False)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for r in range(len(ql)):
+        sl = slice(int(cu[r]), int(cu[r + 1]))
+        oa, la = _run_varlen(q[sl], k[sl], v[sl], [0, ql[r]], [0, ql[r]], 0.1, False)
+        assert torch.equal(oa, out[sl]) and torch.equal(la, lse[sl])
+    perm = [2, 0, 3, 1]
+    qp = torch.cat([q[int(cu[r]):int(cu[r + 1])] for r in perm])
+    kp = torch.cat([k[int(cu[r]):int(cu[r + 1])] for r in perm])
+    vp = torch.cat([v[int(cu[r]):int(cu[r + 1])] for r in perm])
+    cup = oracle.cu_seqlens_from_lengths([ql[r] for r in perm])
+    op, _ = _run_varlen(qp, kp, vp, cup, cup, 0.1, False)
+    for i, r in enumerate(perm):
+        assert torch.equal(op[int(cup[i]):int(cup[i + 1])], out[int(cu[r]):int(cu[r + 1])])
+
+
+def _pipeline(inp):
+    """The hot path on the GPU: boundaries from the text mask and grids, joint
+    pack of q/k/v, varlen attention, unpack of the outputs."""
+    H, D = inp.spec.H, inp.spec.D
+    T = inp.total_tokens
+    mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
+    hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV).reshape(-1, 2)
+    cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
+    packed = []
+    for txt, img in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img), (inp.v_text, inp.v_img)):
+        dst = torch.empty((T, H, D), dtype=inp.dtype, device=DEV)
+        vl.pack_by_cu_seqlens(txt.to(DEV), cu_t, dst, dst_row_offsets=cu_j[:-1])
+        vl.pack_by_cu_seqlens(img.to(DEV), cu_i, dst, dst_row_offsets=img_dst)
+        packed.append(dst)
+    q, k, v = packed
+    max_len = inp.max_len
+    fn = vl.varlen_attn_fwd_f32 if inp.dtype == torch.float32 else vl.varlen_attn_fwd
+    out, lse = fn(q, k, v, cu_j, cu_j, max_len, max_len, inp.scale, return_lse=True)
+    out_txt = torch.empty_like(inp.q_text, device=DEV)
+    out_img = torch.empty_like(inp.q_img, device=DEV)
+    vl.unpack_by_cu_seqlens(out, cu_t, out_txt, src_row_offsets=cu_j[:-1])
+    vl.unpack_by_cu_seqlens(out, cu_i, out_img, src_row_offsets=img_dst)
+    torch.cuda.synchronize()
+    return dict(cu=cu_j, q=q, k=k, v=v, out=out, lse=lse, out_txt=out_txt, out_img=out_img)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_configs_sampled(cfg):
+    log(f"[pipeline] config {cfg}: generating inputs")
+    inp = wl.make_varlen_inputs(wl.CONFIGS[cfg], torch.bfloat16)
+    log(f"[pipeline] config {cfg}: T={inp.total_tokens} running GPU path")
+    res = _pipeline(inp)
+    cj, ct, ci, idst = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
+    assert np.array_equal(res["cu"].cpu().numpy(), cj.astype(np.int32))
+    T, H, D = inp.total_tokens, inp.spec.H, inp.spec.D
+    qn = np.zeros((T, H, D), dtype=np.float32)
+    kn = np.zeros((T, H, D), dtype=np.float32)
+    vn = np.zeros((T, H, D), dtype=np.float32)
+    for dst, txt, img in ((qn, inp.q_text, inp.q_img), (kn, inp.k_text, inp.k_img), (vn, inp.v_text, inp.v_img)):
+        oracle.pack_by_cu_seqlens(txt.float().numpy(), ct, dst_row_offsets=cj[:-1], dst=dst)
+        oracle.pack_by_cu_seqlens(img.float().numpy(), ci, dst_row_offsets=idst, dst=dst)
+    # pack is bit-exact on the full tensors
+    assert np.array_equal(res["q"].float().cpu().numpy(), qn)
+    assert np.array_equal(res["k"].float().cpu().numpy(), kn)
+    assert np.array_equal(res["v"].float().cpu().numpy(), vn)
+    rows = sample_rows(cj)
+    log(f"[pipeline] config {cfg}: oracle on {rows.size} sampled rows")
+    ro, rl = oracle.varlen_attention(qn, kn, vn, cj, cj, inp.scale, rows=rows)
+    out = res["out"].float().cpu().numpy()[rows].astype(np.float64)
+    mx, mean = check_close(out, ro, False, f"config {cfg}")
+    check_lse(res["lse"].cpu().numpy()[rows].astype(np.float64), rl, False, f"config {cfg}")
+    log(f"   max-abs {mx:.3g} mean-abs {mean:.3g}")
+    # unpack is the exact inverse on the real rows and zero on the padding
+    out_full = res["out"].cpu()
+    ref_txt = oracle.unpack_by_cu_seqlens(out_full.view(torch.int16).numpy(), ct, wl.TEXT_CAP,
+                                          src_row_offsets=cj[:-1])
+    assert np.array_equal(res["out_txt"].cpu().view(torch.int16).numpy(), ref_txt)
+    ref_img = oracle.unpack_by_cu_seqlens(out_full.view(torch.int16).numpy(), ci, inp.img_cap,
+                                          src_row_offsets=idst)
+    assert np.array_equal(res["out_img"].cpu().view(torch.int16).numpy(), ref_img)
+
+
+# ------------------------------------------------------------------ block-local attention
+
+
+@pytest.mark.parametrize("n", [10, 96, 101, 2003])
+@pytest.mark.parametrize("win", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("f32", [False, True])
+def test_block_local_vs_oracle(n, win, f32):
+    dtype = torch.float32 if f32 else torch.bfloat16
+    lb, la = win
+    log(f"[block_local] n={n} win={win} {dtype}")
+    spec = wl.BLOCK_LOCAL_CONFIGS[5]
+    inp = wl.make_block_local_inputs(spec, dtype, n=n, seed=1000 + n)
+    full, out = canary_out(tuple(inp.q.shape), dtype, pad=1)
+    fn = vl.block_local_attn_fwd_f32 if f32 else vl.block_local_attn_fwd
+    _, lse = fn(inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV), spec.block, lb, la, inp.scale, out=out,
+                return_lse=True)
+    torch.cuda.synchronize()
+    assert_canary(full, pad=1)
+    ro, rl = oracle.block_local_attention(to64(inp.q), to64(inp.k), to64(inp.v), spec.block, lb, la, inp.scale)
+    check_close(to64(out), ro, f32, f"block-local n={n} {win}")
+    check_lse(to64(lse), rl, f32, f"block-local n={n} {win}")
+
+
+@pytest.mark.parametrize("case", [(2, 300, 7, 2, 1, 128), (1, 33, 40, 0, 0, 64), (3, 61, 5, 3, 0, 128),
+                                  (1, 500, 24, 30, 30, 64)])
+def test_block_local_other_shapes(case):
+    B, n, block, lb, la, D = case
+    log(f"[block_local] B={B} n={n} block={block} lb={lb} la={la} D={D}")
+    rng = np.random.default_rng(n)
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, n, 2, D)).astype(np.float32)).to(torch.bfloat16)
+               for _ in range(3))
+    out = vl.block_local_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), block, lb, la, wl.softmax_scale(D))
+    ro, _ = oracle.block_local_attention(to64(q), to64(k), to64(v), block, lb, la, wl.softmax_scale(D))
+    check_close(to64(out), ro, False, f"block-local {case}")
+
+
+def test_block_local_own_block_equals_varlen_bitwise_free_check():
+    """Own-block windows with n a multiple of the block are varlen with equal
+    24-token requests: both entry points agree within bf16 tolerance."""
+    log("[block_local] own-block vs varlen")
+    rng = np.random.default_rng(44)
+    n, H, D = 24 * 40, 2, 64
+    q, k, v = (torch.from_numpy(rng.standard_normal((1, n, H, D)).astype(np.float32)).to(torch.bfloat16)
+               for _ in range(3))
+    ob = vl.block_local_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), 24, 0, 0, 0.125)
+    cu = torch.arange(0, n + 1, 24, dtype=torch.int32, device=DEV)
+    ov = vl.varlen_attn_fwd(q[0].to(DEV), k[0].to(DEV), v[0].to(DEV), cu, cu, 24, 24, 0.125)
+    torch.cuda.synchronize()
+    d = (ob[0].float() - ov.float()).abs().max().item()
+    assert d <= 2e-2
+
+
+# ------------------------------------------------------------------ errors
+
+
+def test_error_paths_return_codes():
+    log("[errors]")
+    q = torch.zeros((10, 2, 96), dtype=torch.bfloat16, device=DEV)
+    cu = torch.tensor([0, 10], dtype=torch.int32, device=DEV)
+    with pytest.raises(vl.VarlenError, match="unsupported"):
+        vl.varlen_attn_fwd(q, q, q, cu, cu, 10, 10)
+    q2 = torch.zeros((10, 2, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(vl.VarlenError):
+        vl.varlen_attn_fwd(q2, q2, q2, cu, cu, 10, 10, padded_tokens=4)
+    with pytest.raises(vl.VarlenError):
+        vl.varlen_attn_fwd(q2, q2, q2, cu, cu, 10, 10, attn_mask=torch.ones(1))
+    with pytest.raises(vl.VarlenError, match="invalid"):
+        vl.block_local_attn_fwd(q2[None], q2[None], q2[None], 0, 0, 0)
+    with pytest.raises(vl.VarlenError):
+        vl.varlen_attn_fwd(q2.cpu(), q2.cpu(), q2.cpu(), cu.cpu(), cu.cpu(), 10, 10)
