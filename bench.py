@@ -1,0 +1,262 @@
+"""Benchmark of the packed varlen attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. boundaries (cu_seqlens) from the real text mask and the image grids,
+  2. joint text+image pack of Q, K and V into flat [T, H, D],
+  3. flat varlen attention (bf16 MFMA, fp32 accumulation),
+  4. unpack of the output back to the per-request text / image layout,
+  5. block-local attention of the vocoder-DiT shape (n=2003, 24-frame blocks,
+     H=16, D=64) for each of the four window types (own block, one back,
+     one ahead, both).
+The default workload is the single joint request of a 2048x2048 image
+(16,384 image tokens + 8..256 text tokens, H=24, D=128, bf16).
+
+value = algorithmic FLOP of one step / step time, where the FLOP count is
+4*D*H per in-request (query, key) pair (the varlen pairs plus the in-window
+block-local pairs); work the kernels avoid is never counted.
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(HERE, "profiles")
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+
+def err(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("attn.hip", "vl_device.h"):
+        with open(os.path.join(HERE, "packed_variable_length_varlen_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from committed rocprofv3
+    --pmc counters (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel factor);
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, "varlen_attn_bf16_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("workloads", {}).get(workload, {}).get("hbm_bytes_per_launch")
+
+
+def varlen_pairs(cu) -> int:
+    cu = [int(x) for x in cu]
+    return sum((cu[i + 1] - cu[i]) ** 2 for i in range(len(cu) - 1))
+
+
+def block_local_pairs(n: int, block: int, lb: int, la: int) -> int:
+    nb = (n + block - 1) // block
+    tot = 0
+    for b in range(nb):
+        rows = min(n, (b + 1) * block) - b * block
+        lo = max(0, b - lb) * block
+        hi = min(n, (min(nb - 1, b + la) + 1) * block)
+        tot += rows * (hi - lo)
+    return tot
+
+
+def cpu_baseline(inp, cu_host, budget_s: float = 15.0):
+    """Time the CPU oracle on a bounded sample of the same workload: query rows
+    of the varlen attention, taken in blocks of 128 until ~budget_s has passed.
+    Returns the oracle's throughput in TFLOP/s (same 4*D*H per pair count)."""
+    import oracle  # the reported CPU baseline only
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    H, D = inp.spec.H, inp.spec.D
+    cj, ct, ci, idst = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
+    T = int(cj[-1])
+    packed = []
+    for txt, img in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img), (inp.v_text, inp.v_img)):
+        dst = np.zeros((T, H, D), dtype=np.float32)
+        oracle.pack_by_cu_seqlens(txt.float().numpy(), ct, dst_row_offsets=cj[:-1], dst=dst)
+        oracle.pack_by_cu_seqlens(img.float().numpy(), ci, dst_row_offsets=idst, dst=dst)
+        packed.append(dst)
+    q, k, v = packed
+    rng = np.random.default_rng(0)
+    order = rng.permutation(T)
+    flops = 0.0
+    rows_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and rows_done < T:
+        rows = np.sort(order[rows_done:rows_done + 128])
+        oracle.varlen_attention(q, k, v, cj, cj, inp.scale, rows=rows)
+        req = np.searchsorted(cj, rows, side="right") - 1
+        flops += float(sum(4 * D * H * int(cj[r + 1] - cj[r]) for r in req))
+        rows_done += rows.size
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows_done} of {T} query rows x {H} heads of the varlen attention "
+                      f"(fp64 NumPy oracle, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import packed_variable_length_varlen_amd as vl
+    from packed_variable_length_varlen_amd import workloads as wl
+
+    vl.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    spec = wl.CONFIGS[args.config]
+    err(f"[bench] generating config {args.config} ({spec.name})")
+    inp = wl.make_varlen_inputs(spec, torch.bfloat16)
+    H, D = spec.H, spec.D
+    R = inp.R
+    T = inp.total_tokens
+    max_len = inp.max_len
+
+    # inputs resident in HBM before timing
+    mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(dev)
+    hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=dev).reshape(R, 2)
+    slabs = [(t.to(dev), i.to(dev)) for t, i in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img),
+                                                  (inp.v_text, inp.v_img))]
+    cu_j = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    cu_t = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    cu_i = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    img_dst = torch.empty(R, dtype=torch.int32, device=dev)
+    packed = [torch.empty((T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    out_txt = torch.empty_like(slabs[0][0])
+    out_img = torch.empty_like(slabs[0][1])
+
+    bl_spec = wl.BLOCK_LOCAL_CONFIGS[5]
+    bl = wl.make_block_local_inputs(bl_spec, torch.bfloat16)
+    bq, bk, bv = bl.q.to(dev), bl.k.to(dev), bl.v.to(dev)
+    bouts = [torch.empty_like(bq) for _ in bl_spec.windows]
+
+    stream = torch.cuda.current_stream()
+    ev_attn = []
+
+    def step(record: bool):
+        vl.joint_cu_seqlens(mask_d, hw_d, outs=(cu_j, cu_t, cu_i, img_dst))
+        for (txt, img), dst in zip(slabs, packed):
+            vl.pack_by_cu_seqlens(txt, cu_t, dst, dst_row_offsets=cu_j[:-1])
+            vl.pack_by_cu_seqlens(img, cu_i, dst, dst_row_offsets=img_dst)
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        vl.varlen_attn_fwd(packed[0], packed[1], packed[2], cu_j, cu_j, max_len, max_len, inp.scale, out=out)
+        if record:
+            e1.record(stream)
+            ev_attn.append((e0, e1))
+        vl.unpack_by_cu_seqlens(out, cu_t, out_txt, src_row_offsets=cu_j[:-1])
+        vl.unpack_by_cu_seqlens(out, cu_i, out_img, src_row_offsets=img_dst)
+        for (lb, la), o in zip(bl_spec.windows, bouts):
+            vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o)
+
+    err(f"[bench] T={T} R={R} H={H} D={D}: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    err(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_attn]))
+
+    cu_host = cu_j.cpu().numpy()  # after timing: only for the FLOP count
+    pairs = varlen_pairs(cu_host)
+    bl_pairs = [block_local_pairs(bl_spec.n, bl_spec.block, lb, la) for lb, la in bl_spec.windows]
+    flop_varlen = 4.0 * D * H * pairs
+    flop_bl = 4.0 * bl_spec.D * bl_spec.H * sum(bl_pairs)
+    step_flop = flop_varlen + flop_bl
+    ms_per_step = dt * 1e3 / args.steps
+    value = step_flop / (dt / args.steps) / 1e12
+    achieved = flop_varlen / (attn_ms * 1e-3) / 1e12
+    workload = f"config{args.config}:{spec.name}+blocklocal-n2003-b24-h16-d64-4windows"
+    traffic = load_traffic(f"config{args.config}")
+
+    err(f"[bench] step {ms_per_step:.3f} ms, attention {attn_ms:.3f} ms = {achieved:.1f} TFLOP/s "
+        f"({100 * achieved / BF16_PEAK_TFLOPS:.1f}% of bf16 peak); pairs {pairs}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        err("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(inp, cu_host)
+        err(f"[bench] oracle {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "varlen attention fwd TFLOP/s (in-request pairs) and % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workload,
+            "total_tokens": T,
+            "requests": R,
+            "heads": H,
+            "head_dim": D,
+            "in_request_pairs": pairs,
+            "block_local_pairs": bl_pairs,
+            "pct_of_bf16_peak_step": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_bf16_kernel<128,false> (varlen_attn_fwd)",
+            "kernel_ms": round(attn_ms, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -179,53 +179,71 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[NKB], int key0, int g, i
 
 // ---------------------------------------------------------------- bf16 kernel
 
+// s_waitcnt immediates (gfx9 encoding): wait for all vector-memory operations,
+// or for all LDS / scalar-memory operations.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
 template <int D>
 struct Bf16Geo {
   static constexpr int kThreads = 256;
   static constexpr int BM = 128;
-  static constexpr int BN = 8192 / D;                   // keys per tile
-  static constexpr int kKStride = D * 2 + 16;           // bytes per K row in LDS
-  static constexpr int kKBytes = BN * kKStride;
-  static constexpr int kVtRow = BN * 2;                 // bytes per V^T row
-  static constexpr int kVBytes = D * kVtRow;
-  static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kLdsBytes = 2 * kBufBytes;
-  static constexpr int DCH = D / 8;                     // 16-byte chunks per row
-  static constexpr int kKPasses = BN * DCH / kThreads;
+  static constexpr int BN = 8192 / D;                   // keys per tile (16 KB of K, 16 KB of V)
+  static constexpr int ROW = D * 2;                     // bytes per K / V row in LDS (no padding)
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  static constexpr int kTileBytes = BN * ROW;           // 16 KB
+  static constexpr int RPI = 1024 / ROW;                // rows per wave-wide 16-byte load
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // per tensor, per tile
   static constexpr int NKB = BN / 32;
   static constexpr int NDS = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int NKC = BN / 16;
-  static_assert((BN / 4) * DCH == kThreads, "one V transpose task per thread");
+  static_assert(kLoadsPerWave == 4, "4 wave-wide loads of K and of V per tile");
 };
 
-// 16-byte chunk swizzle of a V^T row: rows d..d+7 read the same logical chunk
-// from 8 different bank groups, and the transposing writes of one wave land
-// at most two to a bank group.
-__device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 3)) & 7; }
+// XOR swizzles of the 16-byte chunks of a K / V row in LDS.  Each row is
+// written whole by one wave-wide load, so any permutation inside a row is
+// free on the write side; on the read side they spread the rows a wave reads
+// together over distinct bank groups.
+//  K: lanes 0..15 read the same logical chunk of 16 consecutive rows.
+//  V: a transposing read covers 64 bytes of 8 consecutive rows.
+template <int CPR>
+__device__ __forceinline__ int k_swz(int r) { return r & (CPR - 1); }
+template <int CPR>
+__device__ __forceinline__ int v_swz(int r) { return (((r >> 1) & 3) << 2) & (CPR - 1); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane
+// group, output lane j element e is element (j mod 4) of the 8 bytes input
+// lane 4e + j/4 points at.
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
 
 template <int D, bool kBlockLocal>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   using G = Bf16Geo<D>;
-  __shared__ __attribute__((aligned(16))) char smem[G::kLdsBytes];
+  // Two separate buffers (not one indexed array) so that the compiler sees
+  // the prefetch into one never aliases the reads of the other.
+  __shared__ __attribute__((aligned(16))) char k0[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v0[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char k1[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
 
   const TileRange tr = tile_range<G::BM, kBlockLocal>(a);
   if (!tr.valid) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31;
   const int g = lane >> 5;
   const int H = a.H;
   const int h = tr.h;
   const int64_t row_stride = (int64_t)H * D;  // elements between consecutive tokens
 
-  const __bf16* __restrict__ qg = (const __bf16*)a.q;
-  const __bf16* __restrict__ kg = (const __bf16*)a.k;
-  const __bf16* __restrict__ vg = (const __bf16*)a.v;
-
-  // Query row of this lane and its key window.
   const int my_row = tr.q0 + wave * 32 + ql;
   const bool row_ok = my_row < tr.q1;
   const bool wave_active = tr.q0 + wave * 32 < tr.q1;
@@ -235,89 +253,108 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     window_of(a, i, lo, hi);
   }
 
+  // Q operand of S^T = K Q^T: lane (ql, g) holds features ds*16 + 8g .. +7.
   bf16x8 qf[G::NDS];
   {
-    const __bf16* qp = qg + (int64_t)my_row * row_stride + (int64_t)h * D + g * 8;
+    const int qrow = min(my_row, tr.q1 - 1);
+    const bf16x8* qp = (const bf16x8*)((const __bf16*)a.q + (int64_t)qrow * row_stride + (int64_t)h * D + g * 8);
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds)
-      qf[ds] = row_ok ? *(const bf16x8*)(qp + ds * 16) : bf16x8{};
+    for (int ds = 0; ds < G::NDS; ++ds) qf[ds] = qp[2 * ds];
+  }
+
+  // Direct global -> LDS copy of one tile: wave w's load i fills LDS bytes
+  // [(4w + i) KB, +1 KB); lane l lands on row (4w+i)*RPI + l/CPR, physical
+  // chunk l % CPR, and so fetches logical chunk (l % CPR) ^ swz(row).
+  const int ld_row_in_blk = lane / G::CPR;
+  const int ld_pchunk = lane % G::CPR;
+  const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
+  uint32_t ld_koff[4], ld_voff[4];
+  int ld_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ld_row[i] = (4 * wave + i) * G::RPI + ld_row_in_blk;
+    ld_koff[i] = (uint32_t)ld_row[i] * rs_bytes + (ld_pchunk ^ k_swz<G::CPR>(ld_row[i])) * 16;
+    ld_voff[i] = (uint32_t)ld_row[i] * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(ld_row[i])) * 16;
+  }
+  const char* kbase = (const char*)a.k + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
+  const char* vbase = (const char*)a.v + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
+
+  auto issue_loads = [&](int tile, char* kdst, char* vdst) {
+    const int key0 = tr.k_lo + tile * G::BN;
+    const int last = tr.k_hi - 1 - key0;  // rows past it re-read it (masked keys)
+    const char* kt = kbase + (int64_t)key0 * rs_bytes;
+    const char* vt = vbase + (int64_t)key0 * rs_bytes;
+    if (last >= G::BN - 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(kt + ld_koff[i]),
+                                         (__attribute__((address_space(3))) void*)(kdst + (4 * wave + i) * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + ld_voff[i]),
+                                         (__attribute__((address_space(3))) void*)(vdst + (4 * wave + i) * 1024),
+                                         16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t back = (uint32_t)(ld_row[i] - min(ld_row[i], last)) * rs_bytes;
+        __builtin_amdgcn_global_load_lds((const void*)(kt + (ld_koff[i] - back)),
+                                         (__attribute__((address_space(3))) void*)(kdst + (4 * wave + i) * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + (ld_voff[i] - back)),
+                                         (__attribute__((address_space(3))) void*)(vdst + (4 * wave + i) * 1024),
+                                         16, 0, 0);
+      }
+    }
+  };
+
+  // Per-lane LDS read offsets.
+  //  K operand (rows = keys, k = features): lane (ql, g), step ds reads
+  //  logical chunk 2ds+g of row kb*32+ql.
+  int k_rd[G::NDS];
+#pragma unroll
+  for (int ds = 0; ds < G::NDS; ++ds) k_rd[ds] = ql * G::ROW + (((2 * ds + g) ^ k_swz<G::CPR>(ql)) * 16);
+  //  V^T operand via transposing reads: in 16-lane group G' (lane-half g =
+  //  G'/2, feature half G' % 2), input lane i points at row 4g + i/4 (and
+  //  + 8 for elements 4..7) of the 16-key chunk, features
+  //  db*32 + 16*(G' % 2) + 4*(i % 4) .. +3.  Element e of output lane j is
+  //  then V[key 4g+e (or 8+4g+e-4)][db*32 + 16*(G'%2) + j], which is the k-slot
+  //  order of the P operand taken from the score registers.
+  const int grp = lane >> 4;
+  const int gi = lane & 15;
+  const int v_row = 4 * (grp >> 1) + (gi >> 2);
+  int v_rd[G::NDB];
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) {
+    const int byte_in_row = db * 64 + 32 * (grp & 1) + 8 * (gi & 3);
+    const int chunk = (byte_in_row >> 4) ^ v_swz<G::CPR>(v_row);
+    v_rd[db] = v_row * G::ROW + chunk * 16 + (byte_in_row & 15);
   }
 
   RowState<G::NKB, G::NDB> st;
   st.init();
 
-  const int nkeys = tr.k_hi - tr.k_lo;
-  const int ntiles = (nkeys + G::BN - 1) / G::BN;
-
-  // Per-thread copy tasks of one tile.
-  u32x4 kr[G::kKPasses];
-  u32x4 vr[4];
-  const int v_dc = tid % G::DCH;   // feature chunk (8 features) of the V task
-  const int v_kg = tid / G::DCH;   // key group (4 keys) of the V task
-
-  auto gload = [&](int tile) {
-    const int key0 = tr.k_lo + tile * G::BN;
-    const int valid = min(G::BN, tr.k_hi - key0);
-    const int64_t base = (int64_t)(tr.kv_base + key0) * row_stride + (int64_t)h * D;
-    // Rows past the last valid key re-read the last valid row: their scores
-    // are masked to -inf, so they carry probability 0 times finite data.
-#pragma unroll
-    for (int p = 0; p < G::kKPasses; ++p) {
-      const int idx = p * G::kThreads + tid;
-      const int row = min(idx / G::DCH, valid - 1);
-      const int ch = idx % G::DCH;
-      kr[p] = *(const u32x4*)(kg + base + (int64_t)row * row_stride + ch * 8);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int row = min(4 * v_kg + c, valid - 1);
-      vr[c] = *(const u32x4*)(vg + base + (int64_t)row * row_stride + v_dc * 8);
-    }
-  };
-
-  auto lstore = [&](int buf) {
-    char* kl = smem + buf * G::kBufBytes;
-    char* vl = kl + G::kKBytes;
-#pragma unroll
-    for (int p = 0; p < G::kKPasses; ++p) {
-      const int idx = p * G::kThreads + tid;
-      const int row = idx / G::DCH;
-      const int ch = idx % G::DCH;
-      *(u32x4*)(kl + row * G::kKStride + ch * 16) = kr[p];
-    }
-    // V^T[d][slot]: keys 4*kg..4*kg+3 of feature d, in the slot order the
-    // P operand expects (bits 2 and 3 of the key index swapped).
-    const int chunk = 2 * (v_kg >> 2) + (v_kg & 1);
-    const int half = (v_kg >> 1) & 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      uint32_t lo2, hi2;
-      if ((e & 1) == 0) {
-        lo2 = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-        hi2 = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
-      } else {
-        lo2 = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-        hi2 = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-      }
-      const int d = 8 * v_dc + e;
-      const int phys = chunk ^ vt_swizzle(d);
-      *(u32x2*)(vl + d * G::kVtRow + phys * 16 + half * 8) = u32x2{lo2, hi2};
-    }
-  };
-
-  auto compute = [&](int buf, int tile, bool masked) {
-    const char* kl = smem + buf * G::kBufBytes;
-    const char* vl = kl + G::kKBytes;
+  auto compute = [&](int tile, const char* kl, const char* vl, bool masked) {
+    // S^T = K Q^T; the K operands of step ds+1 are read while step ds's
+    // MFMAs run (sched_barrier keeps the reads from sinking to their use).
     f32x16 s[G::NKB];
 #pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) {
-      s[kb] = f32x16{};
+    for (int kb = 0; kb < G::NKB; ++kb) s[kb] = f32x16{};
+    bf16x8 ka[2][G::NKB];
 #pragma unroll
-      for (int ds = 0; ds < G::NDS; ++ds) {
-        const bf16x8 ka = *(const bf16x8*)(kl + (kb * 32 + ql) * G::kKStride + ds * 32 + g * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ds], s[kb], 0, 0, 0);
+    for (int kb = 0; kb < G::NKB; ++kb) ka[0][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[0]);
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds) {
+      if (ds + 1 < G::NDS) {
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb)
+          ka[(ds + 1) & 1][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[ds + 1]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds & 1][kb], qf[ds], s[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (masked) mask_scores<G::NKB>(s, tr.k_lo + tile * G::BN, g, lo, hi);
     st.softmax_tile(s, a.c);
@@ -326,30 +363,43 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     for (int kc = 0; kc < G::NKC; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][8 * (kc & 1) + e];
+    // O^T += V^T P^T, V^T operands one (kc, db) step ahead.
+    auto read_v = [&](int kc, int db) {
+      const char* p = vl + kc * 16 * G::ROW + v_rd[db];
+      const i16x4 lo4 = lds_read_tr(p);
+      const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 va[2];
+    va[0] = read_v(0, 0);
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-      const int d = db * 32 + ql;
-      const char* vrow = vl + d * G::kVtRow;
-      const int sw = vt_swizzle(d);
-#pragma unroll
-      for (int kc = 0; kc < G::NKC; ++kc) {
-        const bf16x8 va = *(const bf16x8*)(vrow + (((2 * kc + g) ^ sw) * 16));
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kc], st.o[db], 0, 0, 0);
-      }
+    for (int step = 0; step < G::NKC * G::NDB; ++step) {
+      const int kc = step / G::NDB;
+      const int db = step % G::NDB;
+      if (step + 1 < G::NKC * G::NDB) va[(step + 1) & 1] = read_v((step + 1) / G::NDB, (step + 1) % G::NDB);
+      __builtin_amdgcn_sched_barrier(0);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step & 1], pf[kc], st.o[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  const int nkeys = tr.k_hi - tr.k_lo;
+  const int ntiles = (nkeys + G::BN - 1) / G::BN;
   const bool ragged = (nkeys % G::BN) != 0;
-  for (int it = 0; it < ntiles; ++it) {
-    const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1);
-    if (wave_active) compute(it & 1, it, kBlockLocal || (ragged && !more));
-    if (more) lstore((it + 1) & 1);
+  auto is_masked = [&](int tile) { return kBlockLocal || (ragged && tile == ntiles - 1); };
+
+  if (ntiles > 0) issue_loads(0, k0, v0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) issue_loads(it + 1, k1, v1);
+    if (wave_active) compute(it, k0, v0, is_masked(it));
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (it + 2 < ntiles) issue_loads(it + 2, k0, v0);
+    if (wave_active) compute(it + 1, k1, v1, is_masked(it + 1));
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
 
