@@ -183,6 +183,8 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[NKB], int key0, int g, i
 // or for all LDS / scalar-memory operations.
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
+// Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 struct Bf16Geo {
@@ -206,11 +208,12 @@ struct Bf16Geo {
 // free on the write side; on the read side they spread the rows a wave reads
 // together over distinct bank groups.
 //  K: lanes 0..15 read the same logical chunk of 16 consecutive rows.
-//  V: a transposing read covers 64 bytes of 8 consecutive rows.
+//  V: a transposing read covers 64 bytes of each of 8 consecutive rows;
+//     rows 4k..4k+3 are moved 0 / 64 / 128 / 192 bytes apart.
 template <int CPR>
 __device__ __forceinline__ int k_swz(int r) { return r & (CPR - 1); }
 template <int CPR>
-__device__ __forceinline__ int v_swz(int r) { return (((r >> 1) & 3) << 2) & (CPR - 1); }
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) & (CPR - 1); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -269,42 +272,32 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   const int ld_pchunk = lane % G::CPR;
   const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
   uint32_t ld_koff[4], ld_voff[4];
-  int ld_row[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ld_row[i] = (4 * wave + i) * G::RPI + ld_row_in_blk;
-    ld_koff[i] = (uint32_t)ld_row[i] * rs_bytes + (ld_pchunk ^ k_swz<G::CPR>(ld_row[i])) * 16;
-    ld_voff[i] = (uint32_t)ld_row[i] * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(ld_row[i])) * 16;
+    const int row = (4 * wave + i) * G::RPI + ld_row_in_blk;
+    ld_koff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ k_swz<G::CPR>(row)) * 16;
+    ld_voff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(row)) * 16;
   }
   const char* kbase = (const char*)a.k + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
   const char* vbase = (const char*)a.v + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
 
+  // Buffer descriptors cover only the tile's valid rows, so the hardware
+  // range check returns zeros for rows past the sequence end (their scores
+  // are masked).  MUBUF loads (not FLAT) keep LDS waits precise.
   auto issue_loads = [&](int tile, char* kdst, char* vdst) {
     const int key0 = tr.k_lo + tile * G::BN;
-    const int last = tr.k_hi - 1 - key0;  // rows past it re-read it (masked keys)
-    const char* kt = kbase + (int64_t)key0 * rs_bytes;
-    const char* vt = vbase + (int64_t)key0 * rs_bytes;
-    if (last >= G::BN - 1) {
+    const int valid = min(G::BN, tr.k_hi - key0);
+    const int nbytes = (valid - 1) * (int)rs_bytes + G::ROW;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)key0 * rs_bytes), 0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)key0 * rs_bytes), 0, nbytes, kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_global_load_lds((const void*)(kt + ld_koff[i]),
-                                         (__attribute__((address_space(3))) void*)(kdst + (4 * wave + i) * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + ld_voff[i]),
-                                         (__attribute__((address_space(3))) void*)(vdst + (4 * wave + i) * 1024),
-                                         16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t back = (uint32_t)(ld_row[i] - min(ld_row[i], last)) * rs_bytes;
-        __builtin_amdgcn_global_load_lds((const void*)(kt + (ld_koff[i] - back)),
-                                         (__attribute__((address_space(3))) void*)(kdst + (4 * wave + i) * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + (ld_voff[i] - back)),
-                                         (__attribute__((address_space(3))) void*)(vdst + (4 * wave + i) * 1024),
-                                         16, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + (4 * wave + i) * 1024),
+                                               16, ld_koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + (4 * wave + i) * 1024),
+                                               16, ld_voff[i], 0, 0, 0);
     }
   };
 
@@ -340,20 +333,23 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     f32x16 s[G::NKB];
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb) s[kb] = f32x16{};
-    bf16x8 ka[2][G::NKB];
+    constexpr int KPF = 2;  // K operand steps read ahead of their MFMAs
+    bf16x8 ka[KPF + 1][G::NKB];
 #pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) ka[0][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[0]);
+    for (int ds = 0; ds < KPF; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb) ka[ds][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[ds]);
 #pragma unroll
     for (int ds = 0; ds < G::NDS; ++ds) {
-      if (ds + 1 < G::NDS) {
+      if (ds + KPF < G::NDS) {
 #pragma unroll
         for (int kb = 0; kb < G::NKB; ++kb)
-          ka[(ds + 1) & 1][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[ds + 1]);
+          ka[(ds + KPF) % (KPF + 1)][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[ds + KPF]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < G::NKB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds & 1][kb], qf[ds], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][kb], qf[ds], s[kb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (masked) mask_scores<G::NKB>(s, tr.k_lo + tile * G::BN, g, lo, hi);
@@ -370,15 +366,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
       const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 va[2];
-    va[0] = read_v(0, 0);
+    constexpr int VPF = 3;  // V operand steps read ahead of their MFMAs
+    constexpr int NSTEP = G::NKC * G::NDB;
+    bf16x8 va[VPF + 1];
 #pragma unroll
-    for (int step = 0; step < G::NKC * G::NDB; ++step) {
+    for (int step = 0; step < VPF; ++step) va[step] = read_v(step / G::NDB, step % G::NDB);
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
       const int kc = step / G::NDB;
       const int db = step % G::NDB;
-      if (step + 1 < G::NKC * G::NDB) va[(step + 1) & 1] = read_v((step + 1) / G::NDB, (step + 1) % G::NDB);
+      if (step + VPF < NSTEP) va[(step + VPF) % (VPF + 1)] = read_v((step + VPF) / G::NDB, (step + VPF) % G::NDB);
       __builtin_amdgcn_sched_barrier(0);
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step & 1], pf[kc], st.o[db], 0, 0, 0);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[kc], st.o[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
