@@ -262,7 +262,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_bf16_kernel<128,false> (varlen_attn_fwd)",
+            "kernel": "attn_bf16_kernel<128, 4, 1, 64, false> (varlen_attn_fwd)",
             "kernel_ms": round(attn_ms, 4),
         },
         "cpu_baseline": cpu,

@@ -179,28 +179,25 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[NKB], int key0, int g, i
 
 // ---------------------------------------------------------------- bf16 kernel
 
-// s_waitcnt immediates (gfx9 encoding): wait for all vector-memory operations,
-// or for all LDS / scalar-memory operations.
+// s_waitcnt immediate (gfx9 encoding) that waits for all vector-memory operations.
 constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitLgkm0 = 0xC07F;
 // Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
-template <int D>
+template <int D, int WAVES, int BN_>
 struct Bf16Geo {
-  static constexpr int kThreads = 256;
-  static constexpr int BM = 128;
-  static constexpr int BN = 8192 / D;                   // keys per tile (16 KB of K, 16 KB of V)
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int BN = BN_;                        // keys per tile
   static constexpr int ROW = D * 2;                     // bytes per K / V row in LDS (no padding)
   static constexpr int CPR = D / 8;                     // 16-byte chunks per row
-  static constexpr int kTileBytes = BN * ROW;           // 16 KB
+  static constexpr int kTileBytes = BN * ROW;
   static constexpr int RPI = 1024 / ROW;                // rows per wave-wide 16-byte load
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // per tensor, per tile
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / WAVES;  // per tensor, per tile
   static constexpr int NKB = BN / 32;
   static constexpr int NDS = D / 16;
   static constexpr int NDB = D / 32;
   static constexpr int NKC = BN / 16;
-  static_assert(kLoadsPerWave == 4, "4 wave-wide loads of K and of V per tile");
+  static_assert(kLoadsPerWave * WAVES * 1024 == kTileBytes, "whole wave-wide loads per tile");
 };
 
 // XOR swizzles of the 16-byte chunks of a K / V row in LDS.  Each row is
@@ -215,6 +212,21 @@ __device__ __forceinline__ int k_swz(int r) { return r & (CPR - 1); }
 template <int CPR>
 __device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) & (CPR - 1); }
 
+// Copies N wave-wide 16-byte-per-lane rows of a tile straight into LDS
+// (buffer_load ... lds): load i lands at lds + i KB, lane l at +16*l; lane l
+// fetches base + voff[i].  The buffer descriptor spans nbytes from base, so
+// reads past it return zeros.  Device pass only.
+template <int N>
+__device__ __forceinline__ void lds_dma_tile(const char* base, int nbytes, char* lds, const uint32_t (&voff)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds + i * 1024), 16,
+                                             voff[i], 0, 0, 0);
+#endif
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -225,9 +237,15 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-template <int D, bool kBlockLocal>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
-  using G = Bf16Geo<D>;
+// QB = query blocks of 32 rows per wave, BN = keys per tile.  With QB = 2
+// every K and V operand read from LDS feeds two MFMAs, which halves LDS read
+// traffic per FLOP (LDS bandwidth, especially the transposing V reads, is the
+// co-limiter at 32 rows per wave); such a wave takes one SIMD's whole register
+// file, and 32-key tiles keep its two score buffers within it.
+template <int D, int WAVES, int QB, int BN, bool kBlockLocal>
+__global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kernel(AttnArgs a) {
+  using G = Bf16Geo<D, WAVES, BN>;
+  constexpr int BM = 32 * QB * WAVES;
   // Two separate buffers (not one indexed array) so that the compiler sees
   // the prefetch into one never aliases the reads of the other.
   __shared__ __attribute__((aligned(16))) char k0[G::kTileBytes];
@@ -235,7 +253,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k1[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
 
-  const TileRange tr = tile_range<G::BM, kBlockLocal>(a);
+  const TileRange tr = tile_range<BM, kBlockLocal>(a);
   if (!tr.valid) return;
 
   const int tid = threadIdx.x;
@@ -247,34 +265,44 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   const int h = tr.h;
   const int64_t row_stride = (int64_t)H * D;  // elements between consecutive tokens
 
-  const int my_row = tr.q0 + wave * 32 + ql;
-  const bool row_ok = my_row < tr.q1;
-  const bool wave_active = tr.q0 + wave * 32 < tr.q1;
-  int lo = tr.k_lo, hi = tr.k_hi;
-  if (kBlockLocal) {
-    const int i = min(tr.seq_q0 + wave * 32 + ql, a.n - 1);
-    window_of(a, i, lo, hi);
+  // Query rows of this lane: block b of the wave covers rows
+  // wave*32*QB + 32b .. +31 of the tile.
+  const int wave_row0 = tr.q0 + wave * 32 * QB;
+  const bool wave_active = wave_row0 < tr.q1;
+  int my_row[QB];
+  int lo[QB], hi[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    my_row[b] = wave_row0 + 32 * b + ql;
+    lo[b] = tr.k_lo;
+    hi[b] = tr.k_hi;
+    if (kBlockLocal) {
+      const int i = min(tr.seq_q0 + wave * 32 * QB + 32 * b + ql, a.n - 1);
+      window_of(a, i, lo[b], hi[b]);
+    }
   }
 
   // Q operand of S^T = K Q^T: lane (ql, g) holds features ds*16 + 8g .. +7.
-  bf16x8 qf[G::NDS];
-  {
-    const int qrow = min(my_row, tr.q1 - 1);
+  bf16x8 qf[QB][G::NDS];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int qrow = min(my_row[b], tr.q1 - 1);
     const bf16x8* qp = (const bf16x8*)((const __bf16*)a.q + (int64_t)qrow * row_stride + (int64_t)h * D + g * 8);
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) qf[ds] = qp[2 * ds];
+    for (int ds = 0; ds < G::NDS; ++ds) qf[b][ds] = qp[2 * ds];
   }
 
   // Direct global -> LDS copy of one tile: wave w's load i fills LDS bytes
-  // [(4w + i) KB, +1 KB); lane l lands on row (4w+i)*RPI + l/CPR, physical
-  // chunk l % CPR, and so fetches logical chunk (l % CPR) ^ swz(row).
+  // [(L*w + i) KB, +1 KB) (L loads per wave); lane l lands on row
+  // (L*w+i)*RPI + l/CPR, physical chunk l % CPR, and so fetches logical chunk
+  // (l % CPR) ^ swz(row).
   const int ld_row_in_blk = lane / G::CPR;
   const int ld_pchunk = lane % G::CPR;
   const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
-  uint32_t ld_koff[4], ld_voff[4];
+  uint32_t ld_koff[G::kLoadsPerWave], ld_voff[G::kLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (4 * wave + i) * G::RPI + ld_row_in_blk;
+  for (int i = 0; i < G::kLoadsPerWave; ++i) {
+    const int row = (G::kLoadsPerWave * wave + i) * G::RPI + ld_row_in_blk;
     ld_koff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ k_swz<G::CPR>(row)) * 16;
     ld_voff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(row)) * 16;
   }
@@ -284,21 +312,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
   // Buffer descriptors cover only the tile's valid rows, so the hardware
   // range check returns zeros for rows past the sequence end (their scores
   // are masked).  MUBUF loads (not FLAT) keep LDS waits precise.
-  auto issue_loads = [&](int tile, char* kdst, char* vdst) {
-    const int key0 = tr.k_lo + tile * G::BN;
-    const int valid = min(G::BN, tr.k_hi - key0);
-    const int nbytes = (valid - 1) * (int)rs_bytes + G::ROW;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)key0 * rs_bytes), 0, nbytes, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)key0 * rs_bytes), 0, nbytes, kBufferFlags);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kdst + (4 * wave + i) * 1024),
-                                               16, ld_koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vdst + (4 * wave + i) * 1024),
-                                               16, ld_voff[i], 0, 0, 0);
-    }
+  auto tile_bytes = [&](int tile) {
+    const int valid = min(G::BN, tr.k_hi - (tr.k_lo + tile * G::BN));
+    return (valid - 1) * (int)rs_bytes + G::ROW;
+  };
+  auto issue_k = [&](int tile, char* kdst) {
+    lds_dma_tile<G::kLoadsPerWave>(kbase + (int64_t)(tr.k_lo + tile * G::BN) * rs_bytes, tile_bytes(tile),
+                                   kdst + G::kLoadsPerWave * wave * 1024, ld_koff);
+  };
+  auto issue_v = [&](int tile, char* vdst) {
+    lds_dma_tile<G::kLoadsPerWave>(vbase + (int64_t)(tr.k_lo + tile * G::BN) * rs_bytes, tile_bytes(tile),
+                                   vdst + G::kLoadsPerWave * wave * 1024, ld_voff);
   };
 
   // Per-lane LDS read offsets.
@@ -324,102 +348,200 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs a) {
     v_rd[db] = v_row * G::ROW + chunk * 16 + (byte_in_row & 15);
   }
 
-  RowState<G::NKB, G::NDB> st;
-  st.init();
-
-  auto compute = [&](int tile, const char* kl, const char* vl, bool masked) {
-    // S^T = K Q^T; the K operands of step ds+1 are read while step ds's
-    // MFMAs run (sched_barrier keeps the reads from sinking to their use).
-    f32x16 s[G::NKB];
+  RowState<G::NKB, G::NDB> st[QB];
 #pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) s[kb] = f32x16{};
-    constexpr int KPF = 2;  // K operand steps read ahead of their MFMAs
-    bf16x8 ka[KPF + 1][G::NKB];
-#pragma unroll
-    for (int ds = 0; ds < KPF; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb) ka[ds][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[ds]);
-#pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) {
-      if (ds + KPF < G::NDS) {
-#pragma unroll
-        for (int kb = 0; kb < G::NKB; ++kb)
-          ka[(ds + KPF) % (KPF + 1)][kb] = *(const bf16x8*)(kl + kb * 32 * G::ROW + k_rd[ds + KPF]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][kb], qf[ds], s[kb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (masked) mask_scores<G::NKB>(s, tr.k_lo + tile * G::BN, g, lo, hi);
-    st.softmax_tile(s, a.c);
-    bf16x8 pf[G::NKC];
-#pragma unroll
-    for (int kc = 0; kc < G::NKC; ++kc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][8 * (kc & 1) + e];
-    // O^T += V^T P^T, V^T operands one (kc, db) step ahead.
-    auto read_v = [&](int kc, int db) {
-      const char* p = vl + kc * 16 * G::ROW + v_rd[db];
-      const i16x4 lo4 = lds_read_tr(p);
-      const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    constexpr int VPF = 3;  // V operand steps read ahead of their MFMAs
-    constexpr int NSTEP = G::NKC * G::NDB;
-    bf16x8 va[VPF + 1];
-#pragma unroll
-    for (int step = 0; step < VPF; ++step) va[step] = read_v(step / G::NDB, step % G::NDB);
-#pragma unroll
-    for (int step = 0; step < NSTEP; ++step) {
-      const int kc = step / G::NDB;
-      const int db = step % G::NDB;
-      if (step + VPF < NSTEP) va[(step + VPF) % (VPF + 1)] = read_v((step + VPF) / G::NDB, (step + VPF) % G::NDB);
-      __builtin_amdgcn_sched_barrier(0);
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[kc], st.o[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
+  for (int b = 0; b < QB; ++b) st[b].init();
 
   const int nkeys = tr.k_hi - tr.k_lo;
   const int ntiles = (nkeys + G::BN - 1) / G::BN;
   const bool ragged = (nkeys % G::BN) != 0;
   auto is_masked = [&](int tile) { return kBlockLocal || (ragged && tile == ntiles - 1); };
 
-  if (ntiles > 0) issue_loads(0, k0, v0);
+  // ---- S^T = K Q^T.  Step `step` = (ds, kb) with kb fastest; each K
+  // operand feeds the QB query blocks.
+  constexpr int NSTEP_S = G::NKB * G::NDS;
+  constexpr int KPF = 2;  // K operand steps read ahead of their MFMAs
+  auto read_k = [&](const char* kl, int step) {
+    return *(const bf16x8*)(kl + (step % G::NKB) * 32 * G::ROW + k_rd[step / G::NKB]);
+  };
+  auto qk = [&](const char* kl, f32x16(&s)[QB][G::NKB]) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb) s[b][kb] = f32x16{};
+    bf16x8 ka[KPF + 1];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) ka[i] = read_k(kl, i);
+#pragma unroll
+    for (int step = 0; step < NSTEP_S; ++step) {
+      if (step + KPF < NSTEP_S) ka[(step + KPF) % (KPF + 1)] = read_k(kl, step + KPF);
+      VL_SCHED_BARRIER(0);
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        s[b][step % G::NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[b][step / G::NKB],
+                                                                     s[b][step % G::NKB], 0, 0, 0);
+      VL_SCHED_BARRIER(0);
+    }
+  };
+
+  // ---- Row max of a block's scores and the lazy rescale; returns -offset.
+  auto row_max = [&](RowState<G::NKB, G::NDB>& rs, f32x16(&s)[G::NKB]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    mx = pair_max(mx);
+    const float mx_c = mx * a.c;
+    const bool need = mx_c > rs.m_c + 8.0f;
+    if (__ballot(need)) {
+      const float m_new = need ? mx_c : rs.m_c;
+      const float alpha = need ? __builtin_amdgcn_exp2f(rs.m_c - m_new) : 1.0f;
+      rs.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < G::NDB; ++d) rs.o[d] *= alpha;
+      rs.m_c = m_new;
+    }
+    return (rs.m_c == -INFINITY) ? 0.f : -rs.m_c;
+  };
+
+  // ---- exp2 / row sum / bf16 conversion of this tile's scores into the P
+  // operands, interleaved with the S MFMAs of the next tile: per S step, one
+  // K read, QB MFMAs and the VALU work of QB * kScoresPerStep scores.  On a
+  // sequence's last tile the next-tile product reads a stale buffer and is
+  // never used; keeping it makes the exp work and the MFMAs one block.
+  auto softmax_qk = [&](f32x16(&sc)[QB][G::NKB], bf16x8(&pf)[QB][G::NKC], const float(&negm)[QB],
+                        const char* kl_next, f32x16(&sn)[QB][G::NKB]) {
+    constexpr int kScoresPerStep = G::NKB * 16 / NSTEP_S;  // each lane holds NKB*16 scores per block
+    static_assert(kScoresPerStep * NSTEP_S == G::NKB * 16, "whole scores per step");
+    float ls[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      ls[b] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb) sn[b][kb] = f32x16{};
+    }
+    bf16x8 ka[KPF + 1];
+#pragma unroll
+    for (int i = 0; i < KPF; ++i) ka[i] = read_k(kl_next, i);
+#pragma unroll
+    for (int step = 0; step < NSTEP_S; ++step) {
+      if (step + KPF < NSTEP_S) ka[(step + KPF) % (KPF + 1)] = read_k(kl_next, step + KPF);
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        sn[b][step % G::NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[b][step / G::NKB],
+                                                                      sn[b][step % G::NKB], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int t = 0; t < kScoresPerStep; ++t) {
+          const int idx = step * kScoresPerStep + t;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[b][idx >> 4][idx & 15], a.c, negm[b]));
+          sc[b][idx >> 4][idx & 15] = p;
+          ls[b] += p;
+          if ((idx & 7) == 7) {
+            const int kc = idx >> 3;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[b][kc][e] = (__bf16)sc[b][kc >> 1][8 * (kc & 1) + e];
+          }
+        }
+      VL_SCHED_GROUP(0x008, QB, 0);                        // the step's MFMAs
+      VL_SCHED_GROUP(0x100, 1, 0);                         // 1 LDS read
+      VL_SCHED_GROUP(0x002, 3 * kScoresPerStep * QB, 0);   // the scores' VALU work
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) st[b].l += ls[b];
+  };
+
+  // ---- O^T += V^T P^T, V^T operands VPF steps ahead, each feeding QB MFMAs.
+  auto read_v = [&](const char* vl, int kc, int db) {
+    const char* p = vl + kc * 16 * G::ROW + v_rd[db];
+    const i16x4 lo4 = lds_read_tr(p);
+    const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv = [&](const char* vl, const bf16x8(&pf)[QB][G::NKC]) {
+    constexpr int VPF = 3;
+    constexpr int NSTEP = G::NKC * G::NDB;
+    bf16x8 va[VPF + 1];
+#pragma unroll
+    for (int step = 0; step < VPF; ++step) va[step] = read_v(vl, step / G::NDB, step % G::NDB);
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
+      if (step + VPF < NSTEP)
+        va[(step + VPF) % (VPF + 1)] = read_v(vl, (step + VPF) / G::NDB, (step + VPF) % G::NDB);
+      VL_SCHED_BARRIER(0);
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        st[b].o[step % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[step % (VPF + 1)], pf[b][step / G::NDB], st[b].o[step % G::NDB], 0, 0, 0);
+      VL_SCHED_BARRIER(0);
+    }
+  };
+
+  // One tile: S of this tile is in sc; K of the next tile is in kl_next
+  // (when there is one), V of this tile in vl.
+  bf16x8 pf[QB][G::NKC];
+  auto tile_step = [&](int tile, f32x16(&sc)[QB][G::NKB], f32x16(&sn)[QB][G::NKB], const char* kl_next,
+                       const char* vl) {
+    float negm[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      if (is_masked(tile)) mask_scores<G::NKB>(sc[b], tr.k_lo + tile * G::BN, g, lo[b], hi[b]);
+      negm[b] = row_max(st[b], sc[b]);
+    }
+    softmax_qk(sc, pf, negm, kl_next, sn);
+    pv(vl, pf);
+  };
+
+  // K runs one tile ahead of V: during tile t the waves read K(t+1) and V(t)
+  // while K(t+2) and V(t+1) stream into the buffers that held K(t) and
+  // V(t-1); one barrier per tile separates the two.
+  f32x16 sA[QB][G::NKB], sB[QB][G::NKB];
+  if (ntiles > 0) {
+    issue_k(0, k0);
+    issue_v(0, v0);
+  }
+  if (ntiles > 1) issue_k(1, k1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
+  if (wave_active && ntiles > 0) qk(k0, sA);
+  __syncthreads();
   for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) issue_loads(it + 1, k1, v1);
-    if (wave_active) compute(it, k0, v0, is_masked(it));
+    if (it + 2 < ntiles) issue_k(it + 2, k0);
+    if (it + 1 < ntiles) issue_v(it + 1, v1);
+    if (wave_active) tile_step(it, sA, sB, k1, v0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (it + 1 >= ntiles) break;
-    if (it + 2 < ntiles) issue_loads(it + 2, k0, v0);
-    if (wave_active) compute(it + 1, k1, v1, is_masked(it + 1));
+    if (it + 3 < ntiles) issue_k(it + 3, k1);
+    if (it + 2 < ntiles) issue_v(it + 2, v0);
+    if (wave_active) tile_step(it + 1, sB, sA, k0, v1);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
 
   if (!wave_active) return;
-  const float l_tot = pair_sum(st.l);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (row_ok) {
-    __bf16* op = (__bf16*)a.out + (int64_t)my_row * row_stride + (int64_t)h * D;
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
+  for (int b = 0; b < QB; ++b) {
+    const float l_tot = pair_sum(st[b].l);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (my_row[b] < tr.q1) {
+      __bf16* op = (__bf16*)a.out + (int64_t)my_row[b] * row_stride + (int64_t)h * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = db * 32 + 8 * i + 4 * g;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 w;
+      for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[db][4 * i + e] * inv);
-        *(bf16x4*)(op + d) = w;
-      }
-    if (a.lse != nullptr && g == 0)
-      a.lse[(int64_t)my_row * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int d = db * 32 + 8 * i + 4 * g;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st[b].o[db][4 * i + e] * inv);
+          *(bf16x4*)(op + d) = w;
+        }
+      if (a.lse != nullptr && g == 0)
+        a.lse[(int64_t)my_row[b] * H + h] = l_tot > 0.f ? (st[b].m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -587,12 +709,11 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- tile-map export
 
-template <int BM>
 __global__ void __launch_bounds__(64) tile_map_kernel(const int32_t* q_cu, const int32_t* kv_cu,
-                                                      int R, int H, int chunk, int32_t* out) {
+                                                      int R, int H, int block_m, int chunk, int32_t* out) {
   const int logical = block_to_logical(blockIdx.x, chunk);
   int req, head, qt;
-  find_tile(q_cu, kv_cu, R, H, BM, logical, req, head, qt);
+  find_tile(q_cu, kv_cu, R, H, block_m, logical, req, head, qt);
   if (threadIdx.x == 0) {
     out[3 * (int64_t)blockIdx.x + 0] = req;
     out[3 * (int64_t)blockIdx.x + 1] = req < 0 ? -1 : head;
@@ -607,8 +728,28 @@ __global__ void __launch_bounds__(64) tile_map_kernel(const int32_t* q_cu, const
 namespace {
 
 constexpr int kChunk = 16;  // logical tiles kept together on one chiplet
+constexpr int kBf16VarlenWaves = 4;  // waves per work-group of the bf16 varlen kernel
+constexpr int kBf16VarlenQB = 1;     // 32-row query blocks per wave: 128 rows per work-group
+constexpr int kBf16VarlenBN = 64;    // keys per tile of the bf16 varlen kernel
+constexpr int kF32Waves = 4;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The varlen launch for a dtype: query rows per work-group, threads, grid.
+struct VarlenPlan {
+  int block_m;
+  int threads;
+  int64_t blocks;
+};
+
+inline VarlenPlan varlen_plan(bool f32, int64_t num_reqs, int64_t max_q, int64_t H) {
+  VarlenPlan p;
+  const int waves = f32 ? kF32Waves : kBf16VarlenWaves;
+  p.block_m = 32 * waves * (f32 ? 1 : kBf16VarlenQB);
+  p.threads = 64 * waves;
+  p.blocks = (num_reqs == 0 || max_q == 0) ? 0 : vl::grid_blocks(num_reqs, max_q, H, p.block_m, kChunk);
+  return p;
+}
 
 int launch_status() {
   return hipGetLastError() == hipSuccess ? VL_OK : VL_ELAUNCH;
@@ -624,7 +765,8 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   if (!q || !k || !v || !q_cu || !kv_cu || !out) return VL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
   if (!(scale == scale)) return VL_EINVAL;
-  const int64_t G = vl::grid_blocks(num_reqs, max_q, H, 128, kChunk);
+  const VarlenPlan plan = varlen_plan(kF32, num_reqs, max_q, H);
+  const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
   vl::AttnArgs a{};
   a.q = q;
@@ -641,14 +783,16 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   (void)hipGetLastError();
   if (kF32) {
     if (D == 128)
-      hipLaunchKernelGGL((vl::attn_f32_kernel<128, false>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_f32_kernel<128, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
     else
-      hipLaunchKernelGGL((vl::attn_f32_kernel<64, false>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_f32_kernel<64, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<128, false>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_bf16_kernel<128, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads), 0,
+                         stream, a);
     else
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<64, false>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_bf16_kernel<64, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads), 0,
+                         stream, a);
   }
   return launch_status();
 }
@@ -689,9 +833,9 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<128, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_bf16_kernel<128, 4, 1, 64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_bf16_kernel<64, 4, 1, 64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
   }
   return launch_status();
 }
@@ -733,12 +877,12 @@ int block_local_attn_fwd_f32(const float* q, const float* k, const float* v, int
 
 int varlen_launch_shape(int32_t max_q, int32_t num_reqs, int32_t H, int32_t D, int dtype_f32,
                         int32_t* block_m, int32_t* chunk, int64_t* blocks) {
-  (void)dtype_f32;
   if (max_q < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
-  if (block_m) *block_m = 128;
+  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, num_reqs, max_q, H);
+  if (block_m) *block_m = plan.block_m;
   if (chunk) *chunk = kChunk;
-  if (blocks) *blocks = (num_reqs == 0 || max_q == 0) ? 0 : vl::grid_blocks(num_reqs, max_q, H, 128, kChunk);
+  if (blocks) *blocks = plan.blocks;
   return VL_OK;
 }
 
@@ -746,14 +890,15 @@ int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, i
                     int32_t num_reqs, int32_t H, int32_t D, int dtype_f32, int32_t* triples_out,
                     int64_t max_blocks, vl_stream_t stream) {
   int64_t G = 0;
-  const int rc = varlen_launch_shape(max_q, num_reqs, H, D, dtype_f32, nullptr, nullptr, &G);
+  int32_t bm = 0;
+  const int rc = varlen_launch_shape(max_q, num_reqs, H, D, dtype_f32, &bm, nullptr, &G);
   if (rc != VL_OK) return rc;
   if (G == 0) return VL_OK;
   if (!q_cu_seqlens || !kv_cu_seqlens || !triples_out || max_blocks < G) return VL_EINVAL;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((vl::tile_map_kernel<128>), dim3((unsigned)G), dim3(64), 0, (hipStream_t)stream,
-                     q_cu_seqlens, kv_cu_seqlens, num_reqs, H, kChunk, triples_out);
+  hipLaunchKernelGGL(vl::tile_map_kernel, dim3((unsigned)G), dim3(64), 0, (hipStream_t)stream, q_cu_seqlens,
+                     kv_cu_seqlens, num_reqs, H, bm, kChunk, triples_out);
   return launch_status();
 }
 

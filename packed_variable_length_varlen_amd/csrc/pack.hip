@@ -92,28 +92,53 @@ __global__ void __launch_bounds__(256) cu_from_lengths_kernel(const int32_t* __r
   }
 }
 
-// One 256-thread block: text lengths from the mask, image tokens from the
-// grids, and the joint / text / image boundaries plus each image segment's
-// first packed row.
+// Number of nonzero bytes of request r's mask row, summed by one wave
+// (4-byte words when the row is word-aligned, else bytes).  Wave-uniform.
+__device__ __forceinline__ int wave_count_nonzero(const uint8_t* __restrict__ row, int cap) {
+  const int lane = lane_id();
+  int cnt = 0;
+  if ((cap & 3) == 0 && (((uintptr_t)row) & 3) == 0) {
+    const uint32_t* w = (const uint32_t*)row;
+    for (int i = lane; i < cap / 4; i += 64) {
+      const uint32_t x = w[i];
+      cnt += ((x & 0xffu) != 0) + ((x & 0xff00u) != 0) + ((x & 0xff0000u) != 0) + ((x & 0xff000000u) != 0);
+    }
+  } else {
+    for (int i = lane; i < cap; i += 64) cnt += row[i] != 0;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+  return cnt;
+}
+
+// One 256-thread block: text lengths from the mask (one wave per request),
+// image tokens from the grids, and the joint / text / image boundaries plus
+// each image segment's first packed row, 256 requests at a time.
 __global__ void __launch_bounds__(256) joint_cu_kernel(const uint8_t* __restrict__ mask,
                                                        int text_cap, const int32_t* __restrict__ hw,
                                                        int R, int32_t* cu_joint, int32_t* cu_text,
                                                        int32_t* cu_img, int32_t* img_dst) {
   __shared__ int lds8[8];
   __shared__ int carry[3];
+  __shared__ int tlen[256];
+  const int wave = threadIdx.x >> 6;
   if (threadIdx.x < 3) carry[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     if (cu_joint) cu_joint[0] = 0;
     if (cu_text) cu_text[0] = 0;
     if (cu_img) cu_img[0] = 0;
   }
-  __syncthreads();
   for (int r0 = 0; r0 < R; r0 += 256) {
+    const int nr = min(256, R - r0);
+    for (int i = wave; i < nr; i += 4) {
+      const int c = text_cap > 0 ? wave_count_nonzero(mask + (int64_t)(r0 + i) * text_cap, text_cap) : 0;
+      if (lane_id() == 0) tlen[i] = c;
+    }
+    __syncthreads();
     const int r = r0 + threadIdx.x;
     int t = 0, n = 0;
     if (r < R) {
-      const uint8_t* m = mask + (int64_t)r * text_cap;
-      for (int j = 0; j < text_cap; ++j) t += m[j] != 0;
+      t = tlen[threadIdx.x];
       n = hw[2 * r] * hw[2 * r + 1];
     }
     const int it = block_scan_256(t, lds8);

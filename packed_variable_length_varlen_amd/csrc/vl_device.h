@@ -6,6 +6,16 @@
 
 #include "../../include/varlen.h"
 
+// Instruction-scheduling hints; they only mean something in the device pass
+// (the host pass of a kernel template must not see the gfx builtins).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define VL_SCHED_BARRIER(mask) __builtin_amdgcn_sched_barrier(mask)
+#define VL_SCHED_GROUP(mask, n, id) __builtin_amdgcn_sched_group_barrier(mask, n, id)
+#else
+#define VL_SCHED_BARRIER(mask)
+#define VL_SCHED_GROUP(mask, n, id)
+#endif
+
 namespace vl {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
