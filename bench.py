@@ -177,25 +177,35 @@ def main():
     bouts = [torch.empty_like(bq) for _ in bl_spec.windows]
 
     stream = torch.cuda.current_stream()
-    ev_attn = []
+    ev = {"attn": [], "pack": [], "unpack": [], "blocal": []}
+
+    def mark(record):
+        if not record:
+            return None
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
 
     def step(record: bool):
         vl.joint_cu_seqlens(mask_d, hw_d, outs=(cu_j, cu_t, cu_i, img_dst))
+        e0 = mark(record)
         for (txt, img), dst in zip(slabs, packed):
             vl.pack_by_cu_seqlens(txt, cu_t, dst, dst_row_offsets=cu_j[:-1])
             vl.pack_by_cu_seqlens(img, cu_i, dst, dst_row_offsets=img_dst)
-        if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+        e1 = mark(record)
         vl.varlen_attn_fwd(packed[0], packed[1], packed[2], cu_j, cu_j, max_len, max_len, inp.scale, out=out)
-        if record:
-            e1.record(stream)
-            ev_attn.append((e0, e1))
+        e2 = mark(record)
         vl.unpack_by_cu_seqlens(out, cu_t, out_txt, src_row_offsets=cu_j[:-1])
         vl.unpack_by_cu_seqlens(out, cu_i, out_img, src_row_offsets=img_dst)
+        e3 = mark(record)
         for (lb, la), o in zip(bl_spec.windows, bouts):
             vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o)
+        e4 = mark(record)
+        if record:
+            ev["pack"].append((e0, e1))
+            ev["attn"].append((e1, e2))
+            ev["unpack"].append((e2, e3))
+            ev["blocal"].append((e3, e4))
 
     err(f"[bench] T={T} R={R} H={H} D={D}: warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -209,7 +219,16 @@ def main():
         step(True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_attn]))
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    attn_ms = ms["attn"]
+    row_bytes = H * D * 2
+    real_rows = sum(inp.text_len) + sum(inp.img_tokens)
+    pack_bytes = 3 * 2 * real_rows * row_bytes
+    unpack_bytes = real_rows * row_bytes + R * (wl.TEXT_CAP + inp.img_cap) * row_bytes
+    err(f"[bench] pack q/k/v: {ms['pack']*1e3:.1f} us, {pack_bytes/ms['pack']/1e6:.0f} GB/s "
+        f"({100*pack_bytes/ms['pack']/1e6/HBM_PEAK_GBS:.1f}% of HBM); unpack out: {ms['unpack']*1e3:.1f} us, "
+        f"{unpack_bytes/ms['unpack']/1e6:.0f} GB/s ({100*unpack_bytes/ms['unpack']/1e6/HBM_PEAK_GBS:.1f}% of HBM); "
+        f"block-local x4: {ms['blocal']*1e3:.1f} us")
 
     cu_host = cu_j.cpu().numpy()  # after timing: only for the FLOP count
     pairs = varlen_pairs(cu_host)

@@ -85,6 +85,26 @@ int unpack_by_cu_seqlens(const void* src_flat, const int32_t* src_row_offsets,
                          const int32_t* cu_seqlens, int32_t num_reqs, int64_t row_bytes,
                          void* dst_padded, int64_t max_len, int zero_fill, vl_stream_t stream);
 
+/* unpack_cfg_combine: per-request classifier-free-guidance combine fused into
+ *   the unpack (vLLM-Omni PR #4024, "CFG behavior": the combine
+ *   negative + true_cfg_scale * (positive - negative) is applied after the
+ *   per-request split, and requests with different scales batch together).
+ *   Request r has a positive and a negative segment of the same length
+ *   len_r = seg_cu[r+1] - seg_cu[r] in the flat buffer, starting at rows
+ *   pos_rows[r] and neg_rows[r]; for i < len_r
+ *     dst[r*max_len + i] = bf16(neg + scale[r] * (pos - neg))
+ *   computed in fp64 and rounded once to bf16 (nearest even), so scale 0 and 1
+ *   return neg and pos bit for bit; rows i >= len_r are zeroed when
+ *   zero_fill != 0.  src_flat, dst_padded:
+ *   bf16 rows of row_elems elements (row_elems % 8 == 0, 16-byte aligned);
+ *   seg_cu int32 [num_reqs+1], pos_rows / neg_rows int32 [num_reqs], scale
+ *   float32 [num_reqs], all device; len_r <= max_len is trusted.
+ */
+int unpack_cfg_combine(const void* src_flat, const int32_t* seg_cu, const int32_t* pos_rows,
+                       const int32_t* neg_rows, const float* scale, int32_t num_reqs,
+                       int64_t row_elems, void* dst_padded, int64_t max_len, int zero_fill,
+                       vl_stream_t stream);
+
 /* ---------------------------------------------------------------- varlen attention
  * varlen_attn_fwd: flat non-causal attention over packed [T, H, D] bf16 Q/K/V
  *   (PR #6711 "Key changes" and "Reference / Acknowledgement"; PR #4024
@@ -128,6 +148,20 @@ int block_local_attn_fwd_f32(const float* q, const float* k, const float* v, int
                              int32_t n, int32_t H, int32_t D, int32_t block, int32_t look_back,
                              int32_t look_ahead, float scale, float* out, float* lse,
                              vl_stream_t stream);
+
+/* ---------------------------------------------------------------- MixFusion layout check (host)
+ * mixfusion_chunk_plan: whether a mixed-resolution batch may take the flat
+ *   varlen layout (vLLM-Omni PR #6711, "How to enable MixFusion": the layout
+ *   is rejected when the gcd of the token counts is below
+ *   mixfusion_min_chunk_tokens, default 256, or when the resulting chunk count
+ *   exceeds mixfusion_max_chunks, default 128).  chunk_size = gcd of the
+ *   counts, chunk_count = sum / chunk_size.  Host-only, no GPU.
+ *   token_counts: int64 [n] (host), n >= 1, every count >= 1.  Writes
+ *   *chunk_size / *chunk_count (may be NULL); returns 1 if accepted, 0 if
+ *   rejected, VL_EINVAL on bad arguments.
+ */
+int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chunk_tokens,
+                         int64_t max_chunks, int64_t* chunk_size, int64_t* chunk_count);
 
 /* ---------------------------------------------------------------- schedule (test export)
  * varlen_launch_shape: host-only; the launch varlen_attn_fwd (dtype_f32 = 0)

@@ -19,7 +19,7 @@ __all__ = [
     "load_library", "lib_path", "cu_seqlens_from_lengths", "joint_cu_seqlens",
     "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "varlen_attn_fwd", "varlen_attn_fwd_f32",
     "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
-    "VarlenError",
+    "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +50,8 @@ _SIGNATURES = {
     "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_int, _vp, _vp, _vp], _c_int),
     "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _vp, _c_i64, _vp],
                         _c_int),
+    "mixfusion_chunk_plan": ([_vp, _c_i32, _c_i64, _c_i64, _vp, _vp], _c_int),
+    "unpack_cfg_combine": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i64, _vp, _c_i64, _c_int, _vp], _c_int),
 }
 
 
@@ -182,6 +184,27 @@ def unpack_by_cu_seqlens(src_flat: torch.Tensor, cu_seqlens: torch.Tensor, dst_p
     return dst_padded
 
 
+def unpack_cfg_combine(src_flat: torch.Tensor, seg_cu: torch.Tensor, pos_rows: torch.Tensor,
+                       neg_rows: torch.Tensor, scale: torch.Tensor, dst_padded: torch.Tensor,
+                       zero_fill: bool = True, stream=None) -> torch.Tensor:
+    """dst_padded[r, i] = neg + scale[r] * (pos - neg) over request r's segments (bf16)."""
+    _gpu(src_flat, "src_flat", torch.bfloat16)
+    _gpu(dst_padded, "dst_padded", torch.bfloat16)
+    for name, t in (("seg_cu", seg_cu), ("pos_rows", pos_rows), ("neg_rows", neg_rows)):
+        _gpu(t, name, torch.int32)
+    _gpu(scale, "scale", torch.float32)
+    R = seg_cu.numel() - 1
+    if pos_rows.numel() != R or neg_rows.numel() != R or scale.numel() != R or dst_padded.shape[0] != R:
+        raise VarlenError("seg_cu [R+1], pos_rows / neg_rows / scale [R] and dst_padded [R, ...] must agree")
+    if tuple(dst_padded.shape[2:]) != tuple(src_flat.shape[1:]):
+        raise VarlenError("dst_padded must be [R, max_len, *row] and src_flat [T, *row]")
+    row_elems = src_flat[0].numel() if src_flat.dim() > 1 else 1
+    _check(load_library().unpack_cfg_combine(_ptr(src_flat), _ptr(seg_cu), _ptr(pos_rows), _ptr(neg_rows),
+                                             _ptr(scale), R, row_elems, _ptr(dst_padded), dst_padded.shape[1],
+                                             1 if zero_fill else 0, _stream(stream)), "unpack_cfg_combine")
+    return dst_padded
+
+
 # ------------------------------------------------------------------ attention
 
 
@@ -302,3 +325,18 @@ def varlen_tile_map(q_cu: torch.Tensor, kv_cu: torch.Tensor, max_q: int, H: int,
     _check(load_library().varlen_tile_map(_ptr(q_cu), _ptr(kv_cu), int(max_q), R, H, D, 1 if f32 else 0,
                                           _ptr(out), max(G, 1), _stream(stream)), "varlen_tile_map")
     return out[:G]
+
+
+# ------------------------------------------------------------------ MixFusion layout check (host)
+
+
+def mixfusion_chunk_plan(token_counts, min_chunk_tokens: int = 256, max_chunks: int = 128):
+    """(accepted, chunk_size, chunk_count) for a mixed-resolution batch (host-only)."""
+    counts = [int(c) for c in token_counts]
+    arr = (ctypes.c_int64 * max(len(counts), 1))(*counts)
+    size, count = ctypes.c_int64(), ctypes.c_int64()
+    rc = load_library().mixfusion_chunk_plan(ctypes.cast(arr, ctypes.c_void_p), len(counts), int(min_chunk_tokens),
+                                             int(max_chunks), ctypes.byref(size), ctypes.byref(count))
+    if rc < 0:
+        _check(rc, "mixfusion_chunk_plan")
+    return bool(rc), size.value, count.value

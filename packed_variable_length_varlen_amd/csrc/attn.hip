@@ -227,6 +227,14 @@ __device__ __forceinline__ void lds_dma_tile(const char* base, int nbytes, char*
 #endif
 }
 
+// One wave-wide 16-byte-per-lane copy into LDS (see lds_dma_tile).
+__device__ __forceinline__ void lds_dma_one(const char* base, int nbytes, char* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#endif
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -360,7 +368,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
   // ---- S^T = K Q^T.  Step `step` = (ds, kb) with kb fastest; each K
   // operand feeds the QB query blocks.
   constexpr int NSTEP_S = G::NKB * G::NDS;
-  constexpr int KPF = 2;  // K operand steps read ahead of their MFMAs
+  constexpr int KPF = 3;  // K operand steps read ahead of their MFMAs
   auto read_k = [&](const char* kl, int step) {
     return *(const bf16x8*)(kl + (step % G::NKB) * 32 * G::ROW + k_rd[step / G::NKB]);
   };
@@ -411,9 +419,10 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
   // sequence's last tile the next-tile product reads a stale buffer and is
   // never used; keeping it makes the exp work and the MFMAs one block.
   auto softmax_qk = [&](f32x16(&sc)[QB][G::NKB], bf16x8(&pf)[QB][G::NKC], const float(&negm)[QB],
-                        const char* kl_next, f32x16(&sn)[QB][G::NKB]) {
+                        const char* kl_next, f32x16(&sn)[QB][G::NKB], auto&& load_step) {
     constexpr int kScoresPerStep = G::NKB * 16 / NSTEP_S;  // each lane holds NKB*16 scores per block
     static_assert(kScoresPerStep * NSTEP_S == G::NKB * 16, "whole scores per step");
+    static_assert(NSTEP_S >= 2 * G::kLoadsPerWave, "one tile load per S step at most");
     float ls[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -427,6 +436,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
 #pragma unroll
     for (int step = 0; step < NSTEP_S; ++step) {
       if (step + KPF < NSTEP_S) ka[(step + KPF) % (KPF + 1)] = read_k(kl_next, step + KPF);
+      const bool dma = load_step(step);
 #pragma unroll
       for (int b = 0; b < QB; ++b)
         sn[b][step % G::NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[b][step / G::NKB],
@@ -447,6 +457,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
         }
       VL_SCHED_GROUP(0x008, QB, 0);                        // the step's MFMAs
       VL_SCHED_GROUP(0x100, 1, 0);                         // 1 LDS read
+      if (dma) VL_SCHED_GROUP(0x020, 1, 0);                // 1 tile load into LDS
       VL_SCHED_GROUP(0x002, 3 * kScoresPerStep * QB, 0);   // the scores' VALU work
     }
 #pragma unroll
@@ -461,7 +472,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto pv = [&](const char* vl, const bf16x8(&pf)[QB][G::NKC]) {
-    constexpr int VPF = 3;
+    constexpr int VPF = 6;
     constexpr int NSTEP = G::NKC * G::NDB;
     bf16x8 va[VPF + 1];
 #pragma unroll
@@ -482,15 +493,34 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
   // One tile: S of this tile is in sc; K of the next tile is in kl_next
   // (when there is one), V of this tile in vl.
   bf16x8 pf[QB][G::NKC];
+  // The wave's share of the next tiles' loads (K of tile kt into kdst, V of
+  // tile vt into vdst; -1 = none) is spread one load per S step so the
+  // copies stream while the MFMAs run instead of stalling issue in a burst.
   auto tile_step = [&](int tile, f32x16(&sc)[QB][G::NKB], f32x16(&sn)[QB][G::NKB], const char* kl_next,
-                       const char* vl) {
+                       const char* vl, int kt, char* kdst, int vt, char* vdst) {
     float negm[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       if (is_masked(tile)) mask_scores<G::NKB>(sc[b], tr.k_lo + tile * G::BN, g, lo[b], hi[b]);
       negm[b] = row_max(st[b], sc[b]);
     }
-    softmax_qk(sc, pf, negm, kl_next, sn);
+    const char* ksrc = kbase + (int64_t)(tr.k_lo + kt * G::BN) * rs_bytes;
+    const char* vsrc = vbase + (int64_t)(tr.k_lo + vt * G::BN) * rs_bytes;
+    const int kbytes = kt >= 0 ? tile_bytes(kt) : 0;
+    const int vbytes = vt >= 0 ? tile_bytes(vt) : 0;
+    auto load_step = [&](int step) {
+      constexpr int L = G::kLoadsPerWave;
+      if (step < L) {
+        if (kt >= 0) lds_dma_one(ksrc, kbytes, kdst + (L * wave + step) * 1024, ld_koff[step]);
+        return true;
+      }
+      if (step < 2 * L) {
+        if (vt >= 0) lds_dma_one(vsrc, vbytes, vdst + (L * wave + step - L) * 1024, ld_voff[step - L]);
+        return true;
+      }
+      return false;
+    };
+    softmax_qk(sc, pf, negm, kl_next, sn, load_step);
     pv(vl, pf);
   };
 
@@ -508,15 +538,29 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
   if (wave_active && ntiles > 0) qk(k0, sA);
   __syncthreads();
   for (int it = 0; it < ntiles; it += 2) {
-    if (it + 2 < ntiles) issue_k(it + 2, k0);
-    if (it + 1 < ntiles) issue_v(it + 1, v1);
-    if (wave_active) tile_step(it, sA, sB, k1, v0);
+    {
+      const int kt = it + 2 < ntiles ? it + 2 : -1;
+      const int vt = it + 1 < ntiles ? it + 1 : -1;
+      if (wave_active) {
+        tile_step(it, sA, sB, k1, v0, kt, k0, vt, v1);
+      } else {
+        if (kt >= 0) issue_k(kt, k0);
+        if (vt >= 0) issue_v(vt, v1);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (it + 1 >= ntiles) break;
-    if (it + 3 < ntiles) issue_k(it + 3, k1);
-    if (it + 2 < ntiles) issue_v(it + 2, v0);
-    if (wave_active) tile_step(it + 1, sB, sA, k0, v1);
+    {
+      const int kt = it + 3 < ntiles ? it + 3 : -1;
+      const int vt = it + 2 < ntiles ? it + 2 : -1;
+      if (wave_active) {
+        tile_step(it + 1, sB, sA, k0, v1, kt, k1, vt, v0);
+      } else {
+        if (kt >= 0) issue_k(kt, k1);
+        if (vt >= 0) issue_v(vt, v0);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }

@@ -12,7 +12,7 @@
 namespace vl {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyUnroll = 8;  // independent 16-byte loads in flight per thread
 constexpr int kUnitsPerBlock = kCopyThreads * kCopyUnroll;
 
 // Request r = blockIdx.y copies units [0, len_r*row_units) of its slab in
@@ -45,10 +45,64 @@ __global__ void __launch_bounds__(kCopyThreads) copy_segments_kernel(
     const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
     buf[i] = u < real_units ? s[u] : U{};
   }
+  // Streaming stores: the destination is not re-read by this kernel.
 #pragma unroll
   for (int i = 0; i < kCopyUnroll; ++i) {
     const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
-    if (u < span_units) d[u] = buf[i];
+    if (u < span_units) __builtin_nontemporal_store(buf[i], d + u);
+  }
+}
+
+// fp64 -> bf16 with a single rounding (nearest even): round to odd into fp32,
+// which keeps every discarded bit as a sticky bit, then nearest-even to bf16.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
+  const float f = (float)x;
+  uint32_t b = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != x) {
+    if (fabs(back) > fabs(x)) b -= 1u;  // the value truncated toward zero
+    b |= 1u;
+  }
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)__uint_as_float(b));
+}
+
+// CFG combine fused into unpack: request r = blockIdx.y, 8 bf16 elements
+// (16 bytes) per unit.  dst = neg + s * (pos - neg) in fp64: the difference of
+// two bf16 values is exact there (unless their exponents lie more than 45
+// apart), so the result is rounded once, and scale 0 / 1 return neg / pos
+// bit for bit.  In fp32 the difference rounds as soon as the exponents lie
+// more than 16 apart, and scale 1 then misses pos by an ulp.
+__global__ void __launch_bounds__(kCopyThreads) cfg_combine_kernel(
+    const u32x4* __restrict__ src, const int32_t* __restrict__ seg_cu, const int32_t* __restrict__ pos_rows,
+    const int32_t* __restrict__ neg_rows, const float* __restrict__ scale, int64_t row_units,
+    u32x4* __restrict__ dst, int64_t slab_rows, int zero_tail) {
+  const int r = blockIdx.y;
+  const int64_t len = (int64_t)(seg_cu[r + 1] - seg_cu[r]);
+  const int64_t real_units = len * row_units;
+  const int64_t span_units = zero_tail ? slab_rows * row_units : real_units;
+  const int64_t u0 = (int64_t)blockIdx.x * kUnitsPerBlock;
+  if (u0 >= span_units) return;
+  const u32x4* ps = src + (int64_t)pos_rows[r] * row_units;
+  const u32x4* ns = src + (int64_t)neg_rows[r] * row_units;
+  u32x4* d = dst + (int64_t)r * slab_rows * row_units;
+  const double s = (double)scale[r];
+#pragma unroll
+  for (int i = 0; i < kCopyUnroll; ++i) {
+    const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
+    if (u >= span_units) continue;
+    u32x4 y = u32x4{};
+    if (u < real_units) {
+      const u32x4 p = ps[u];
+      const u32x4 n = ns[u];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // two bf16 per word, widened exactly
+        const double p0 = (double)__uint_as_float(p[w] << 16), p1 = (double)__uint_as_float(p[w] & 0xffff0000u);
+        const double n0 = (double)__uint_as_float(n[w] << 16), n1 = (double)__uint_as_float(n[w] & 0xffff0000u);
+        y[w] = f64_to_bf16_bits(fma(s, p0 - n0, n0)) | (f64_to_bf16_bits(fma(s, p1 - n1, n1)) << 16);
+      }
+    }
+    __builtin_nontemporal_store(y, d + u);
   }
 }
 
@@ -213,6 +267,28 @@ extern "C" {
 
 int vl_version(void) { return 100; }
 
+int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chunk_tokens,
+                         int64_t max_chunks, int64_t* chunk_size, int64_t* chunk_count) {
+  if (!token_counts || n < 1) return VL_EINVAL;
+  int64_t g = 0, total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t c = token_counts[i];
+    if (c < 1) return VL_EINVAL;
+    int64_t a = g, b = c;
+    while (b != 0) {
+      const int64_t t = a % b;
+      a = b;
+      b = t;
+    }
+    g = a;
+    total += c;
+  }
+  const int64_t count = total / g;
+  if (chunk_size) *chunk_size = g;
+  if (chunk_count) *chunk_count = count;
+  return (g >= min_chunk_tokens && count <= max_chunks) ? 1 : 0;
+}
+
 const char* vl_status_string(int status) {
   switch (status) {
     case VL_OK: return "ok";
@@ -221,6 +297,25 @@ const char* vl_status_string(int status) {
     case VL_ELAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
+}
+
+int unpack_cfg_combine(const void* src_flat, const int32_t* seg_cu, const int32_t* pos_rows,
+                       const int32_t* neg_rows, const float* scale, int32_t num_reqs,
+                       int64_t row_elems, void* dst_padded, int64_t max_len, int zero_fill,
+                       vl_stream_t stream) {
+  if (num_reqs < 0 || num_reqs > kMaxReqs || row_elems <= 0 || max_len < 0) return VL_EINVAL;
+  if (row_elems % 8 != 0) return VL_EUNSUPPORTED;
+  if (num_reqs == 0 || max_len == 0) return VL_OK;
+  if (!src_flat || !seg_cu || !pos_rows || !neg_rows || !scale || !dst_padded) return VL_EINVAL;
+  if ((((uintptr_t)src_flat) | ((uintptr_t)dst_padded)) & 15u) return VL_EINVAL;
+  const int64_t row_units = row_elems / 8;
+  const int64_t bx = (max_len * row_units + vl::kUnitsPerBlock - 1) / vl::kUnitsPerBlock;
+  if (bx > INT32_MAX) return VL_EUNSUPPORTED;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(vl::cfg_combine_kernel, dim3((unsigned)bx, (unsigned)num_reqs), dim3(vl::kCopyThreads), 0,
+                     (hipStream_t)stream, (const vl::u32x4*)src_flat, seg_cu, pos_rows, neg_rows, scale, row_units,
+                     (vl::u32x4*)dst_padded, max_len, zero_fill);
+  return launch_status();
 }
 
 int cu_seqlens_from_lengths(const int32_t* lengths, int32_t num_reqs, int32_t* cu_out,

@@ -395,3 +395,104 @@ def test_error_paths_return_codes():
         vl.block_local_attn_fwd(q2[None], q2[None], q2[None], 0, 0, 0)
     with pytest.raises(vl.VarlenError):
         vl.varlen_attn_fwd(q2.cpu(), q2.cpu(), q2.cpu(), cu.cpu(), cu.cpu(), 10, 10)
+
+
+# ------------------------------------------------------------------ CFG combine fused into unpack
+
+
+def _bf16_ulp(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+@pytest.mark.parametrize("row_elems", [3072, 8])
+def test_unpack_cfg_combine_vs_oracle(row_elems):
+    log(f"[cfg] row {row_elems}")
+    rng = np.random.default_rng(row_elems)
+    # sequences [r1+, r1-, r2+, r2-, r3+, r3-]: text of differing length, then an image
+    # segment whose length the positive and negative pass of a request share.
+    img = [300, 77, 1]
+    txt = [[20, 3], [9, 1], [0, 5]]
+    seqs = []
+    for r in range(3):
+        for sgn in range(2):
+            seqs.append((txt[r][sgn], img[r]))
+    lengths = [t + n for t, n in seqs]
+    cu = oracle.cu_seqlens_from_lengths(lengths)
+    T = int(cu[-1])
+    flat = torch.from_numpy(rng.standard_normal((T, row_elems)).astype(np.float32)).to(torch.bfloat16)
+    pos_rows = np.array([cu[2 * r] + txt[r][0] for r in range(3)], dtype=np.int32)
+    neg_rows = np.array([cu[2 * r + 1] + txt[r][1] for r in range(3)], dtype=np.int32)
+    seg_cu = oracle.cu_seqlens_from_lengths(img).astype(np.int32)
+    scale = np.array([4.0, 2.5, 7.0], dtype=np.float32)
+    max_len = 310
+    dst = torch.full((3, max_len, row_elems), 5.0, dtype=torch.bfloat16, device=DEV)
+    vl.unpack_cfg_combine(flat.to(DEV), torch.from_numpy(seg_cu).to(DEV), torch.from_numpy(pos_rows).to(DEV),
+                          torch.from_numpy(neg_rows).to(DEV), torch.from_numpy(scale).to(DEV), dst)
+    torch.cuda.synchronize()
+    got = dst.float().cpu().numpy().astype(np.float64)
+    f64 = flat.float().numpy().astype(np.float64)
+    for r in range(3):
+        n = img[r]
+        ref = oracle.cfg_combine(f64[pos_rows[r]:pos_rows[r] + n], f64[neg_rows[r]:neg_rows[r] + n], float(scale[r]))
+        err = np.abs(got[r, :n] - ref)
+        assert np.all(err <= _bf16_ulp(ref)), f"request {r}: max err {err.max()}"
+        assert not got[r, n:].any(), "padding rows must be zero"
+    # scale 0 gives the negative rows and scale 1 the positive rows, bit for bit
+    for s, rows in ((0.0, neg_rows), (1.0, pos_rows)):
+        sc = torch.full((3,), s, dtype=torch.float32, device=DEV)
+        vl.unpack_cfg_combine(flat.to(DEV), torch.from_numpy(seg_cu).to(DEV), torch.from_numpy(pos_rows).to(DEV),
+                              torch.from_numpy(neg_rows).to(DEV), sc, dst)
+        torch.cuda.synchronize()
+        for r in range(3):
+            a = dst[r, :img[r]].cpu()
+            b = flat[rows[r]:rows[r] + img[r]]
+            if not torch.equal(a, b):
+                bad = (a != b).nonzero()
+                log(f"scale {s} request {r}: {bad.shape[0]} mismatches, first {bad[:4].tolist()}, "
+                    f"got {a[tuple(bad[0])].item()} want {b[tuple(bad[0])].item()}")
+            assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ SP pad tails and production block-local
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_sp_padded_queries_attend_real_keys_only(f32):
+    """Sequence-parallel auto-pad (PR #4293): the query side covers the padded
+    length, the key side only the real tokens, so the pad never changes a real
+    row's output and needs no attention mask."""
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[sp-pad] {dtype}")
+    real = [6889, 1000, 4095]
+    padded = [oracle.sp_auto_pad(n, 8)[0] for n in real]
+    assert padded[0] == 6896
+    q, k, v = wl.random_varlen_case(91, padded, 2, 128, dtype, real)
+    q_cu = oracle.cu_seqlens_from_lengths(padded)
+    kv_cu = oracle.cu_seqlens_from_lengths(real)
+    out, lse = _run_varlen(q, k, v, q_cu, kv_cu, wl.softmax_scale(128), f32)
+    rows = sample_rows(q_cu, n_random=128)
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), q_cu, kv_cu, wl.softmax_scale(128), rows=rows)
+    check_close(to64(out)[rows], ro, f32, "sp pad")
+    check_lse(to64(lse)[rows], rl, f32, "sp pad")
+    # the real rows equal an unpadded run over the same real tokens
+    keep = np.concatenate([np.arange(q_cu[r], q_cu[r] + real[r]) for r in range(3)])
+    o2, _ = _run_varlen(q[torch.from_numpy(keep)], k, v, kv_cu, kv_cu, wl.softmax_scale(128), f32)
+    assert torch.equal(out[torch.from_numpy(keep).to(out.device)].cpu(), o2.cpu())
+
+
+@pytest.mark.parametrize("f32", [True, False])
+def test_block_local_production_shape(f32):
+    """Token2Wav DiT shape of PR #7975: fp32, CFG as batch 2, 4000 mel frames
+    (167 blocks of 24, last block 16 frames), own-block and one-neighbour layers."""
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[block_local] production shape {dtype}")
+    spec = wl.BLOCK_LOCAL_CONFIGS[5]
+    inp = wl.make_block_local_inputs(spec, dtype, n=4000, B=2, seed=4000)
+    for lb, la in [(0, 0), (1, 0), (0, 1)]:
+        out = vl.block_local_attn_fwd_f32(inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV), 24, lb, la, inp.scale) if f32 \
+            else vl.block_local_attn_fwd(inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV), 24, lb, la, inp.scale)
+        torch.cuda.synchronize()
+        ro, _ = oracle.block_local_attention(to64(inp.q), to64(inp.k), to64(inp.v), 24, lb, la, inp.scale)
+        check_close(to64(out), ro, f32, f"production block-local ({lb},{la})")

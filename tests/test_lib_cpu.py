@@ -87,3 +87,20 @@ def test_launch_shape_matches_schedule_spec(lib, max_q, R, H, D):
     expect = oracle.grid_blocks(R, max_q, H, bm, chunk) if max_q > 0 and R > 0 else 0
     assert G == expect
     assert G % (8 * chunk) == 0
+
+
+def test_mixfusion_plan_native_matches_oracle_and_pages(lib):
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "mixfusion_plan_caseB.json")))
+    e = g["expected"]
+    got = vl.mixfusion_chunk_plan(g["token_counts"], g["min_chunk_tokens"], g["max_chunks"])
+    assert got == (e["accepted"], e["chunk_size"], e["chunk_count"])
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        n = int(rng.integers(1, 9))
+        counts = [int(256 * rng.integers(1, 40) * rng.choice([1, 2, 3])) if rng.random() < 0.7
+                  else int(rng.integers(1, 5000)) for _ in range(n)]
+        assert vl.mixfusion_chunk_plan(counts) == oracle.mixfusion_chunk_plan(counts)
+    with pytest.raises(vl.VarlenError):
+        vl.mixfusion_chunk_plan([5, 0])
