@@ -3,7 +3,8 @@
 One step = one pass of the whole path over one batch of synthetic input:
   1. boundaries (cu_seqlens) from the real text mask and the image grids,
   2. joint text+image pack of Q, K and V into flat [T, H, D],
-  3. flat varlen attention (bf16 MFMA, fp32 accumulation),
+  3. flat varlen attention (bf16 MFMA, fp32 accumulation; the last, partial
+     round of work-groups cut along the keys and merged),
   4. unpack of the output back to the per-request text / image layout,
   5. block-local attention of the vocoder-DiT shape (n=2003, 24-frame blocks,
      H=16, D=64) for each of the four window types (own block, one back,
@@ -171,6 +172,9 @@ def main():
     out_txt = torch.empty_like(slabs[0][0])
     out_img = torch.empty_like(slabs[0][1])
 
+    # partial results of the key split of the last round (allocated once)
+    workspace = torch.empty(max(vl.varlen_split_workspace_bytes(D), 1), dtype=torch.uint8, device=dev)
+
     bl_spec = wl.BLOCK_LOCAL_CONFIGS[5]
     bl = wl.make_block_local_inputs(bl_spec, torch.bfloat16)
     bq, bk, bv = bl.q.to(dev), bl.k.to(dev), bl.v.to(dev)
@@ -193,7 +197,8 @@ def main():
             vl.pack_by_cu_seqlens(txt, cu_t, dst, dst_row_offsets=cu_j[:-1])
             vl.pack_by_cu_seqlens(img, cu_i, dst, dst_row_offsets=img_dst)
         e1 = mark(record)
-        vl.varlen_attn_fwd(packed[0], packed[1], packed[2], cu_j, cu_j, max_len, max_len, inp.scale, out=out)
+        vl.varlen_attn_fwd_split(packed[0], packed[1], packed[2], cu_j, cu_j, max_len, max_len, inp.scale,
+                                 out=out, workspace=workspace)
         e2 = mark(record)
         vl.unpack_by_cu_seqlens(out, cu_t, out_txt, src_row_offsets=cu_j[:-1])
         vl.unpack_by_cu_seqlens(out, cu_i, out_img, src_row_offsets=img_dst)
@@ -281,7 +286,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_bf16_kernel<128, 4, 1, 64, false> (varlen_attn_fwd)",
+            "kernel": "attn_bf16_kernel<128, 4, 1, 64, false> + split_merge_kernel (varlen_attn_fwd_split)",
             "kernel_ms": round(attn_ms, 4),
         },
         "cpu_baseline": cpu,

@@ -3,7 +3,8 @@
  *
  * All tensor pointers are DEVICE pointers owned by the caller.  Every function
  * enqueues its work on `stream` and returns at once: no allocation, no
- * host<->device copy or synchronisation, no global mutable state.  Device-
+ * host<->device copy or synchronisation.  The only state the library keeps is
+ * a per-device cache of one occupancy query (varlen_attn_fwd_split).  Device-
  * resident cu_seqlens are trusted preconditions (checking them would need a
  * device-to-host read); host scalars are validated and a bad one returns an
  * error code before anything is launched.  Return value: VL_OK (0) on success,
@@ -129,6 +130,31 @@ int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
                         int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale,
                         float* out, float* lse, vl_stream_t stream);
 
+/* varlen_attn_fwd_split: varlen_attn_fwd with the last, partial round of
+ *   work-groups cut along the keys (same contract and results up to fp32
+ *   summation order).  With `slots` work-groups resident at once on the
+ *   device and T tiles of 128 query rows, tiles [0, full) run whole, full =
+ *   T - T mod slots (0 if T < slots); when the remaining tail tiles would
+ *   leave at least half of the slots idle, each is cut into
+ *   parts = min(16, slots / tail, max_kv / 256) >= 2 key ranges of whole
+ *   64-key tiles, run as separate work-groups that write unnormalised
+ *   partial results to `workspace`; a second kernel on the same stream
+ *   merges them (log-sum-exp weights) into out / lse.  Without such a tail
+ *   the call is varlen_attn_fwd and `workspace` is not touched.
+ *   workspace: device, 16-byte aligned, at least the bytes
+ *   varlen_split_workspace_bytes reports for D; its contents need no
+ *   initialisation and are scratch after the call.  Two calls that share a
+ *   workspace must be ordered (same stream, or synchronised).  A missing or
+ *   short workspace when a split is possible returns VL_EINVAL.
+ * varlen_split_workspace_bytes: host-only; the workspace size for head size D
+ *   on the current device (0 when no device can be queried).
+ */
+int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
+                          const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
+                          int32_t H, int32_t D, float scale, void* out, float* lse, void* workspace,
+                          int64_t workspace_bytes, vl_stream_t stream);
+int varlen_split_workspace_bytes(int32_t D, int64_t* bytes);
+
 /* ---------------------------------------------------------------- block-local attention
  * block_local_attn_fwd: the block-local ("block-sparse") attention of the
  *   Token2Wav DiT (PR #7975, review of the window code, commit messages,
@@ -164,24 +190,30 @@ int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chu
                          int64_t max_chunks, int64_t* chunk_size, int64_t* chunk_count);
 
 /* ---------------------------------------------------------------- schedule (test export)
- * varlen_launch_shape: host-only; the launch varlen_attn_fwd (dtype_f32 = 0)
- *   or varlen_attn_fwd_f32 (dtype_f32 = 1) uses for these scalars: query rows
- *   per work-group (block_m), chiplet chunk, and the number of work-groups.
- *   Any output pointer may be NULL.
- * varlen_tile_map: writes, for every launched work-group b of that launch, the
- *   (request, head, q-tile) it computes into triples_out[3*b .. 3*b+2], or
- *   (-1, -1, -1) for an idle work-group, using the same device code as the
- *   attention kernel.  triples_out: int32 [max_blocks, 3] (device); max_blocks
+ * varlen_launch_shape: host-only; the launch varlen_attn_fwd (dtype_f32 = 0,
+ *   split = 0), varlen_attn_fwd_split (dtype_f32 = 0, split = 1) or
+ *   varlen_attn_fwd_f32 (dtype_f32 = 1) uses for these scalars: query rows
+ *   per work-group (block_m), chiplet chunk, number of work-groups and the
+ *   slot count of the key split (0 = no split possible).  Any output pointer
+ *   may be NULL.
+ * varlen_tile_map: writes, for every launched work-group b of that launch,
+ *   (request, head, q-tile, part, parts) into items_out[5*b .. 5*b+4]:
+ *   part 0 of 1 for a whole tile, key range `part` of `parts` for a split
+ *   one, all -1 for an idle work-group; it runs the same device code as the
+ *   attention kernel.  items_out: int32 [max_blocks, 5] (device); max_blocks
  *   must be >= the launch size, else VL_EINVAL.
  *   Schedule: requests by key length descending (ties: lower index first) when
  *   num_reqs <= 64, else in index order; heads ascending; q-tiles ascending.
- *   Work-group b runs on chiplet b mod 8 and takes logical tile
- *   ((i div chunk)*8 + b mod 8)*chunk + (i mod chunk) with i = b div 8.
+ *   Work-group b runs on chiplet b mod 8 and takes logical item
+ *   ((i div chunk)*8 + b mod 8)*chunk + (i mod chunk) with i = b div 8;
+ *   logical items [0, full) are the tiles in that order, then item
+ *   full + u is part u mod parts of tile full + u div parts.  Part p of a
+ *   tile with nkt key tiles covers key tiles [p*nkt/parts, (p+1)*nkt/parts).
  */
-int varlen_launch_shape(int32_t max_q, int32_t num_reqs, int32_t H, int32_t D, int dtype_f32,
-                        int32_t* block_m, int32_t* chunk, int64_t* blocks);
-int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, int32_t max_q,
-                    int32_t num_reqs, int32_t H, int32_t D, int dtype_f32, int32_t* triples_out,
+int varlen_launch_shape(int32_t max_q, int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, int dtype_f32,
+                        int split, int32_t* block_m, int32_t* chunk, int64_t* blocks, int32_t* slots);
+int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv,
+                    int32_t num_reqs, int32_t H, int32_t D, int dtype_f32, int split, int32_t* items_out,
                     int64_t max_blocks, vl_stream_t stream);
 
 #ifdef __cplusplus

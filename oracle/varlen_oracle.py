@@ -189,6 +189,8 @@ def unpack_by_cu_seqlens(src_flat, cu_seqlens, max_len: int, src_row_offsets=Non
 
 LPT_MAX_REQS = 64   # requests are visited longest-first only up to this count
 XCDS = 8            # chiplets a launch is dealt across, round-robin by block id
+MAX_SPLIT = 16      # key ranges a tile of the last round is cut into, at most
+MIN_SPLIT_KEYS = 256  # ... and at most max_kv // MIN_SPLIT_KEYS of them
 
 
 def tile_order(q_cu, kv_cu, H: int, block_m: int, lpt_max_reqs: int = LPT_MAX_REQS
@@ -223,19 +225,48 @@ def tile_order(q_cu, kv_cu, H: int, block_m: int, lpt_max_reqs: int = LPT_MAX_RE
     return tiles
 
 
-def grid_blocks(num_reqs: int, max_q: int, H: int, block_m: int, chunk: int, xcds: int = XCDS) -> int:
+def split_plan(T: int, slots: int, max_kv: int) -> Tuple[int, int, int]:
+    """(full, tail, parts) of the key split of the last, partial round.
+
+    With `slots` work-groups resident at once and T tiles, tiles [0, full)
+    run whole, full = T - T mod slots (0 when T < slots).  The tail = T - full
+    remaining tiles are cut into parts = min(MAX_SPLIT, slots // tail,
+    max_kv // MIN_SPLIT_KEYS) key ranges each when that is at least 2, i.e.
+    when the tail would leave at least half of the slots idle; otherwise
+    nothing is split: (T, 0, 1).  slots <= 0 turns the split off.
+    """
+    if slots <= 0 or T <= 0:
+        return T, 0, 1
+    full = (T // slots) * slots if T >= slots else 0
+    tail = T - full
+    if tail == 0:
+        return T, 0, 1
+    parts = min(MAX_SPLIT, slots // tail, max_kv // MIN_SPLIT_KEYS)
+    if parts < 2:
+        return T, 0, 1
+    return full, tail, parts
+
+
+def split_range(nkt: int, part: int, parts: int) -> Tuple[int, int]:
+    """Key tiles [lo, hi) of range `part` of `parts` over nkt key tiles."""
+    return part * nkt // parts, (part + 1) * nkt // parts
+
+
+def grid_blocks(num_reqs: int, max_q: int, H: int, block_m: int, chunk: int, xcds: int = XCDS,
+                slots: int = 0) -> int:
     """Launch size the host derives from scalars only: an upper bound on the
-    tile count, rounded up to a whole number of (xcds x chunk) groups."""
-    upper = num_reqs * H * ((max_q + block_m - 1) // block_m)
+    tile count plus one round of slots when the key split is on, rounded up
+    to a whole number of (xcds x chunk) groups."""
+    upper = num_reqs * H * ((max_q + block_m - 1) // block_m) + max(slots, 0)
     group = xcds * chunk
     return ((upper + group - 1) // group) * group
 
 
 def block_to_logical(b: int, chunk: int, xcds: int = XCDS) -> int:
-    """Launched block id -> logical tile index.
+    """Launched block id -> logical work item.
 
     Block ids are dealt to chiplets round-robin (x = b mod xcds); the i-th
-    block a chiplet receives takes logical tile ((i div chunk) * xcds + x) *
+    block a chiplet receives takes logical item ((i div chunk) * xcds + x) *
     chunk + (i mod chunk), so runs of `chunk` consecutive logical tiles (same
     request and head, hence the same K/V) stay on one chiplet's L2.
     """
@@ -244,17 +275,31 @@ def block_to_logical(b: int, chunk: int, xcds: int = XCDS) -> int:
     return ((i // chunk) * xcds + x) * chunk + (i % chunk)
 
 
-def block_schedule(q_cu, kv_cu, H: int, block_m: int, max_q: int, chunk: int,
-                   lpt_max_reqs: int = LPT_MAX_REQS, xcds: int = XCDS) -> np.ndarray:
-    """(request, head, q-tile) of every launched block, (-1, -1, -1) if idle."""
+def work_items(q_cu, kv_cu, H: int, block_m: int, slots: int = 0, max_kv: int = 0,
+               lpt_max_reqs: int = LPT_MAX_REQS) -> List[Tuple[int, int, int, int, int]]:
+    """Logical list of (request, head, q-tile, part, parts) work items: the
+    tiles of tile_order, with those of the last partial round replaced by
+    their key ranges (split_plan), tile by tile."""
     tiles = tile_order(q_cu, kv_cu, H, block_m, lpt_max_reqs)
+    full, tail, parts = split_plan(len(tiles), slots, max_kv)
+    items = [(r, h, qt, 0, 1) for r, h, qt in tiles[:full]]
+    for r, h, qt in tiles[full:full + tail]:
+        items.extend((r, h, qt, p, parts) for p in range(parts))
+    return items
+
+
+def block_schedule(q_cu, kv_cu, H: int, block_m: int, max_q: int, chunk: int,
+                   lpt_max_reqs: int = LPT_MAX_REQS, xcds: int = XCDS, slots: int = 0,
+                   max_kv: int = 0) -> np.ndarray:
+    """(request, head, q-tile, part, parts) of every launched block, all -1 if idle."""
+    items = work_items(q_cu, kv_cu, H, block_m, slots, max_kv, lpt_max_reqs)
     R = len(validate_cu_seqlens(q_cu)) - 1
-    G = grid_blocks(R, max_q, H, block_m, chunk, xcds)
-    out = np.full((G, 3), -1, dtype=np.int64)
+    G = grid_blocks(R, max_q, H, block_m, chunk, xcds, slots)
+    out = np.full((G, 5), -1, dtype=np.int64)
     for b in range(G):
         t = block_to_logical(b, chunk, xcds)
-        if t < len(tiles):
-            out[b] = tiles[t]
+        if t < len(items):
+            out[b] = items[t]
     return out
 
 

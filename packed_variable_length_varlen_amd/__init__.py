@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "load_library", "lib_path", "cu_seqlens_from_lengths", "joint_cu_seqlens",
-    "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "varlen_attn_fwd", "varlen_attn_fwd_f32",
+    "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "varlen_attn_fwd", "varlen_attn_fwd_split",
+    "varlen_split_workspace_bytes", "varlen_attn_fwd_f32",
     "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
     "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError",
 ]
@@ -47,8 +48,12 @@ _SIGNATURES = {
                               _c_i32, _c_f32, _vp, _vp, _vp], _c_int),
     "block_local_attn_fwd_f32": ([_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                   _c_i32, _c_f32, _vp, _vp, _vp], _c_int),
-    "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_int, _vp, _vp, _vp], _c_int),
-    "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _vp, _c_i64, _vp],
+    "varlen_attn_fwd_split": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                               _vp, _vp, _vp, _c_i64, _vp], _c_int),
+    "varlen_split_workspace_bytes": ([_c_i32, _vp], _c_int),
+    "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _vp, _vp, _vp],
+                            _c_int),
+    "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _c_i64, _vp],
                         _c_int),
     "mixfusion_chunk_plan": ([_vp, _c_i32, _c_i64, _c_i64, _vp, _vp], _c_int),
     "unpack_cfg_combine": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i64, _vp, _c_i64, _c_int, _vp], _c_int),
@@ -216,7 +221,7 @@ def _attn_prep(q, k, v, dtype):
 
 
 def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse, padded_tokens,
-            attn_mask, return_lse, stream):
+            attn_mask, return_lse, stream, workspace=None):
     # The flat path rejects attention masks and needs padded_tokens == 0
     # (vLLM-Omni PR #6711, "Reference / Acknowledgement").
     if attn_mask is not None:
@@ -245,11 +250,26 @@ def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse
         _gpu(lse, "lse", torch.float32)
         if tuple(lse.shape) != (T, H):
             raise VarlenError("lse must be [total_tokens, heads]")
-    rc = getattr(load_library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(q_cu), _ptr(kv_cu), int(max_q),
-                                          int(max_kv), R, H, D, float(scale), _ptr(out), _ptr(lse),
-                                          _stream(stream))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(q_cu), _ptr(kv_cu), int(max_q), int(max_kv), R, H, D, float(scale),
+            _ptr(out), _ptr(lse)]
+    if fn_name == "varlen_attn_fwd_split":
+        need = varlen_split_workspace_bytes(D)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            if stream is not None and stream != torch.cuda.current_stream(q.device):
+                workspace.record_stream(stream)
+        _gpu(workspace, "workspace")
+        args += [_ptr(workspace), workspace.numel() * workspace.element_size()]
+    rc = getattr(load_library(), fn_name)(*args, _stream(stream))
     _check(rc, fn_name)
     return (out, lse) if return_lse else out
+
+
+def varlen_split_workspace_bytes(D: int) -> int:
+    """Workspace bytes varlen_attn_fwd_split needs for head size D on the current device."""
+    n = ctypes.c_int64()
+    _check(load_library().varlen_split_workspace_bytes(int(D), ctypes.byref(n)), "varlen_split_workspace_bytes")
+    return n.value
 
 
 def varlen_attn_fwd(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
@@ -258,6 +278,16 @@ def varlen_attn_fwd(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=N
     """bf16 packed [T, H, D] varlen attention; returns out (and lse if asked)."""
     return _varlen("varlen_attn_fwd", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
                    max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream)
+
+
+def varlen_attn_fwd_split(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
+                          lse=None, workspace: Optional[torch.Tensor] = None, padded_tokens: int = 0,
+                          attn_mask=None, return_lse: bool = False, stream=None):
+    """varlen_attn_fwd with the last partial round cut along the keys; `workspace`
+    (a device buffer of varlen_split_workspace_bytes(D) bytes) is allocated
+    when not given."""
+    return _varlen("varlen_attn_fwd_split", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace)
 
 
 def varlen_attn_fwd_f32(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
@@ -307,23 +337,28 @@ def block_local_attn_fwd_f32(q, k, v, block: int, look_back: int, look_ahead: in
 # ------------------------------------------------------------------ schedule export
 
 
-def varlen_launch_shape(max_q: int, num_reqs: int, H: int, D: int, f32: bool = False) -> Tuple[int, int, int]:
-    bm, ch, nb = _c_i32(), _c_i32(), _c_i64()
-    _check(load_library().varlen_launch_shape(max_q, num_reqs, H, D, 1 if f32 else 0, ctypes.byref(bm),
-                                              ctypes.byref(ch), ctypes.byref(nb)), "varlen_launch_shape")
-    return bm.value, ch.value, nb.value
+def varlen_launch_shape(max_q: int, num_reqs: int, H: int, D: int, f32: bool = False, max_kv: int = 0,
+                        split: bool = False) -> Tuple[int, int, int, int]:
+    """(block_m, chunk, blocks, slots) of the launch for these scalars."""
+    bm, ch, nb, sl = _c_i32(), _c_i32(), _c_i64(), _c_i32()
+    _check(load_library().varlen_launch_shape(int(max_q), int(max_kv), int(num_reqs), int(H), int(D),
+                                              1 if f32 else 0, 1 if split else 0, ctypes.byref(bm),
+                                              ctypes.byref(ch), ctypes.byref(nb), ctypes.byref(sl)),
+           "varlen_launch_shape")
+    return bm.value, ch.value, nb.value, sl.value
 
 
 def varlen_tile_map(q_cu: torch.Tensor, kv_cu: torch.Tensor, max_q: int, H: int, D: int, f32: bool = False,
-                    stream=None) -> torch.Tensor:
-    """[blocks, 3] int32 (request, head, q-tile) per launched work-group, -1 if idle."""
+                    max_kv: int = 0, split: bool = False, stream=None) -> torch.Tensor:
+    """[blocks, 5] int32 (request, head, q-tile, part, parts) per launched work-group, -1 if idle."""
     _gpu(q_cu, "q_cu", torch.int32)
     _gpu(kv_cu, "kv_cu", torch.int32)
     R = q_cu.numel() - 1
-    _, _, G = varlen_launch_shape(max_q, R, H, D, f32)
-    out = torch.empty((max(G, 1), 3), dtype=torch.int32, device=q_cu.device)
-    _check(load_library().varlen_tile_map(_ptr(q_cu), _ptr(kv_cu), int(max_q), R, H, D, 1 if f32 else 0,
-                                          _ptr(out), max(G, 1), _stream(stream)), "varlen_tile_map")
+    _, _, G, _ = varlen_launch_shape(max_q, R, H, D, f32, max_kv, split)
+    out = torch.empty((max(G, 1), 5), dtype=torch.int32, device=q_cu.device)
+    _check(load_library().varlen_tile_map(_ptr(q_cu), _ptr(kv_cu), int(max_q), int(max_kv), R, H, D,
+                                          1 if f32 else 0, 1 if split else 0, _ptr(out), max(G, 1),
+                                          _stream(stream)), "varlen_tile_map")
     return out[:G]
 
 

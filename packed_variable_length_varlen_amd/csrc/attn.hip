@@ -25,6 +25,8 @@
 //  * varlen masks keys only in a request's last, partial tile; block-local
 //    masks each row to [lo, hi) computed from integers (no dense mask, no
 //    device-to-host decision) and loads only the union of the rows' windows.
+#include <mutex>
+
 #include "vl_device.h"
 
 namespace vl {
@@ -48,6 +50,12 @@ struct AttnArgs {
   int look_back;
   int look_ahead;
   int nqt;      // query tiles per (batch, head)
+  // key split of the last round (varlen, bf16): slots = resident
+  // work-groups (0 = no split); ws = partial results, per unit BM rows of
+  // D floats of O, then per unit BM (offset, sum) pairs
+  int slots;
+  int max_kv;
+  float* ws;
 };
 
 // ---------------------------------------------------------------- tile setup
@@ -58,30 +66,39 @@ struct TileRange {
   int kv_base;  // absolute row of key 0 of the sequence
   int k_lo, k_hi;  // keys of the tile, relative to kv_base
   int seq_q0;   // row of q0 inside its sequence (block-local windows)
+  int unit;     // partial-result slot of a split work item, -1 for a whole tile
   bool valid;
 };
 
-template <int BM, bool kBlockLocal>
+template <int BM, int BN, bool kBlockLocal>
 __device__ __forceinline__ TileRange tile_range(const AttnArgs& a) {
   TileRange t;
   t.valid = true;
+  t.unit = -1;
   if (!kBlockLocal) {
     const int logical = block_to_logical(blockIdx.x, a.chunk);
-    int req, head, qt;
-    find_tile(a.q_cu, a.kv_cu, a.R, a.H, BM, logical, req, head, qt);
-    if (req < 0) {
+    const WorkItem w = work_item(a.q_cu, a.kv_cu, a.R, a.H, BM, a.slots, a.max_kv, logical);
+    if (w.req < 0) {
       t.valid = false;
       return t;
     }
-    const int qs = a.q_cu[req];
-    const int qe = a.q_cu[req + 1];
-    t.h = head;
-    t.q0 = qs + qt * BM;
+    const int qs = a.q_cu[w.req];
+    const int qe = a.q_cu[w.req + 1];
+    t.h = w.head;
+    t.q0 = qs + w.qt * BM;
     t.q1 = min(qe, t.q0 + BM);
-    t.kv_base = a.kv_cu[req];
+    t.kv_base = a.kv_cu[w.req];
+    const int kv_len = a.kv_cu[w.req + 1] - t.kv_base;
     t.k_lo = 0;
-    t.k_hi = a.kv_cu[req + 1] - t.kv_base;
-    t.seq_q0 = qt * BM;
+    t.k_hi = kv_len;
+    if (w.unit >= 0) {
+      int lo, hi;
+      split_range((kv_len + BN - 1) / BN, w.part, w.parts, lo, hi);
+      t.k_lo = min(kv_len, lo * BN);
+      t.k_hi = min(kv_len, hi * BN);
+      t.unit = w.unit;
+    }
+    t.seq_q0 = w.qt * BM;
   } else {
     const int id = blockIdx.x;
     const int qt = id % a.nqt;
@@ -227,10 +244,16 @@ __device__ __forceinline__ void lds_dma_tile(const char* base, int nbytes, char*
 #endif
 }
 
-// One wave-wide 16-byte-per-lane copy into LDS (see lds_dma_tile).
+// One wave-wide 16-byte-per-lane copy into LDS (see lds_dma_tile).  base and
+// nbytes must be the same in every lane; they are read from the first lane
+// so the compiler knows the descriptor is uniform (no per-lane loop).
 __device__ __forceinline__ void lds_dma_one(const char* base, int nbytes, char* lds, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, kBufferFlags);
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+  const int un = __builtin_amdgcn_readfirstlane(nbytes);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)ub, 0, un, kBufferFlags);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 #endif
 }
@@ -261,7 +284,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
   __shared__ __attribute__((aligned(16))) char k1[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
 
-  const TileRange tr = tile_range<BM, kBlockLocal>(a);
+  const TileRange tr = tile_range<BM, BN, kBlockLocal>(a);
   if (!tr.valid) return;
 
   const int tid = threadIdx.x;
@@ -423,13 +446,10 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
     constexpr int kScoresPerStep = G::NKB * 16 / NSTEP_S;  // each lane holds NKB*16 scores per block
     static_assert(kScoresPerStep * NSTEP_S == G::NKB * 16, "whole scores per step");
     static_assert(NSTEP_S >= 2 * G::kLoadsPerWave, "one tile load per S step at most");
-    float ls[QB];
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      ls[b] = 0.f;
+    for (int b = 0; b < QB; ++b)
 #pragma unroll
       for (int kb = 0; kb < G::NKB; ++kb) sn[b][kb] = f32x16{};
-    }
     bf16x8 ka[KPF + 1];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) ka[i] = read_k(kl_next, i);
@@ -448,7 +468,6 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
           const int idx = step * kScoresPerStep + t;
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[b][idx >> 4][idx & 15], a.c, negm[b]));
           sc[b][idx >> 4][idx & 15] = p;
-          ls[b] += p;
           if ((idx & 7) == 7) {
             const int kc = idx >> 3;
 #pragma unroll
@@ -458,10 +477,10 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
       VL_SCHED_GROUP(0x008, QB, 0);                        // the step's MFMAs
       VL_SCHED_GROUP(0x100, 1, 0);                         // 1 LDS read
       if (dma) VL_SCHED_GROUP(0x020, 1, 0);                // 1 tile load into LDS
-      VL_SCHED_GROUP(0x002, 3 * kScoresPerStep * QB, 0);   // the scores' VALU work
+      // the scores' VALU work: fma and exp per score, one bf16 pair
+      // conversion per two scores
+      VL_SCHED_GROUP(0x002, (2 * kScoresPerStep + kScoresPerStep / 2) * QB, 0);
     }
-#pragma unroll
-    for (int b = 0; b < QB; ++b) st[b].l += ls[b];
   };
 
   // ---- O^T += V^T P^T, V^T operands VPF steps ahead, each feeding QB MFMAs.
@@ -471,9 +490,17 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
     const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto pv = [&](const char* vl, const bf16x8(&pf)[QB][G::NKC]) {
+  // The row sums of this tile's probabilities (still in the score registers,
+  // which the next tile's scores do not overwrite before its softmax) are
+  // added here, a few per MFMA, where the VALU is otherwise idle.
+  auto pv = [&](const char* vl, const bf16x8(&pf)[QB][G::NKC], const f32x16(&sc)[QB][G::NKB]) {
     constexpr int VPF = 6;
     constexpr int NSTEP = G::NKC * G::NDB;
+    constexpr int kSumPerStep = G::NKB * 16 / NSTEP;
+    static_assert(kSumPerStep * NSTEP == G::NKB * 16, "whole scores per step");
+    float ls[QB][2];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) ls[b][0] = ls[b][1] = 0.f;
     bf16x8 va[VPF + 1];
 #pragma unroll
     for (int step = 0; step < VPF; ++step) va[step] = read_v(vl, step / G::NDB, step % G::NDB);
@@ -486,8 +513,21 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
       for (int b = 0; b < QB; ++b)
         st[b].o[step % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             va[step % (VPF + 1)], pf[b][step / G::NDB], st[b].o[step % G::NDB], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+#pragma unroll
+        for (int t = 0; t < kSumPerStep; ++t) {
+          const int idx = step * kSumPerStep + t;
+          ls[b][t & 1] += sc[b][idx >> 4][idx & 15];
+        }
+        // an opaque use keeps the adds in this step (they would otherwise
+        // sink to the sums' only use after the loop)
+        asm volatile("" : "+v"(ls[b][0]), "+v"(ls[b][1]));
+      }
       VL_SCHED_BARRIER(0);
     }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) st[b].l += ls[b][0] + ls[b][1];
   };
 
   // One tile: S of this tile is in sc; K of the next tile is in kl_next
@@ -504,24 +544,28 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
       if (is_masked(tile)) mask_scores<G::NKB>(sc[b], tr.k_lo + tile * G::BN, g, lo[b], hi[b]);
       negm[b] = row_max(st[b], sc[b]);
     }
-    const char* ksrc = kbase + (int64_t)(tr.k_lo + kt * G::BN) * rs_bytes;
-    const char* vsrc = vbase + (int64_t)(tr.k_lo + vt * G::BN) * rs_bytes;
+    // No next tile (kt or vt < 0): the copy still issues, with a zero-byte
+    // descriptor, so it reads nothing; its destination buffer is not read
+    // during this step.  Keeping it unconditional keeps the whole step one
+    // branch-free region for the instruction-group schedule below.
+    const char* ksrc = kt >= 0 ? kbase + (int64_t)(tr.k_lo + kt * G::BN) * rs_bytes : kbase;
+    const char* vsrc = vt >= 0 ? vbase + (int64_t)(tr.k_lo + vt * G::BN) * rs_bytes : vbase;
     const int kbytes = kt >= 0 ? tile_bytes(kt) : 0;
     const int vbytes = vt >= 0 ? tile_bytes(vt) : 0;
     auto load_step = [&](int step) {
       constexpr int L = G::kLoadsPerWave;
       if (step < L) {
-        if (kt >= 0) lds_dma_one(ksrc, kbytes, kdst + (L * wave + step) * 1024, ld_koff[step]);
+        lds_dma_one(ksrc, kbytes, kdst + (L * wave + step) * 1024, ld_koff[step]);
         return true;
       }
       if (step < 2 * L) {
-        if (vt >= 0) lds_dma_one(vsrc, vbytes, vdst + (L * wave + step - L) * 1024, ld_voff[step - L]);
+        lds_dma_one(vsrc, vbytes, vdst + (L * wave + step - L) * 1024, ld_voff[step - L]);
         return true;
       }
       return false;
     };
     softmax_qk(sc, pf, negm, kl_next, sn, load_step);
-    pv(vl, pf);
+    pv(vl, pf, sc);
   };
 
   // K runs one tile ahead of V: during tile t the waves read K(t+1) and V(t)
@@ -566,6 +610,29 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kerne
   }
 
   if (!wave_active) return;
+  if (!kBlockLocal && tr.unit >= 0) {
+    // Split work item: unnormalised O, the exponent offset and the row sum
+    // go to the unit's partial-result slot for the merge kernel.
+    float* wo = a.ws + (int64_t)tr.unit * BM * D;
+    float2* wml = (float2*)(a.ws + (int64_t)a.slots * BM * D) + (int64_t)tr.unit * BM;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float l_tot = pair_sum(st[b].l);
+      if (my_row[b] < tr.q1) {
+        const int r = my_row[b] - tr.q0;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = db * 32 + 8 * i + 4 * g;
+            *(f32x4*)(wo + (int64_t)r * D + d) =
+                f32x4{st[b].o[db][4 * i], st[b].o[db][4 * i + 1], st[b].o[db][4 * i + 2], st[b].o[db][4 * i + 3]};
+          }
+        if (g == 0) wml[r] = make_float2(st[b].m_c, l_tot);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float l_tot = pair_sum(st[b].l);
@@ -613,7 +680,7 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
   using G = F32Geo<D>;
   __shared__ __attribute__((aligned(16))) char smem[G::kLdsBytes];
 
-  const TileRange tr = tile_range<G::BM, kBlockLocal>(a);
+  const TileRange tr = tile_range<G::BM, G::BN, kBlockLocal>(a);
   if (!tr.valid) return;
 
   const int tid = threadIdx.x;
@@ -751,17 +818,67 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- split merge
+
+// Merges the partial results of the split work items: block b < tail takes
+// tile full + b, whose key ranges ran as units b*parts .. b*parts+parts-1.
+// Per row, with exponent offsets m_p (log2 units) and row sums l_p of the
+// parts: m = max m_p, w_p = 2^(m_p - m), out = sum_p w_p O_p / sum_p w_p l_p,
+// lse = (m + log2 sum_p w_p l_p) ln 2.  Empty parts carry m_p = -inf, l_p = 0.
+template <int D, int BM>
+__global__ void __launch_bounds__(256) split_merge_kernel(AttnArgs a) {
+  const SplitPlan sp = split_plan(total_tiles(a.q_cu, a.R, a.H, BM), a.slots, a.max_kv);
+  if (sp.parts < 2 || (int)blockIdx.x >= sp.tail) return;
+  int req, head, qt;
+  find_tile(a.q_cu, a.kv_cu, a.R, a.H, BM, sp.full + (int)blockIdx.x, req, head, qt);
+  if (req < 0) return;
+  const int q0 = a.q_cu[req] + qt * BM;
+  const int rows = min(a.q_cu[req + 1], q0 + BM) - q0;
+  const int64_t u0 = (int64_t)blockIdx.x * sp.parts;
+  const float2* wml = (const float2*)(a.ws + (int64_t)a.slots * BM * D);
+  const int64_t row_stride = (int64_t)a.H * D;
+  constexpr int C4 = D / 4;  // 4-float groups per row
+  for (int f = threadIdx.x; f < rows * C4; f += 256) {
+    const int r = f / C4;
+    const int c = f % C4;
+    float m = -INFINITY;
+    for (int p = 0; p < sp.parts; ++p) m = fmaxf(m, wml[(u0 + p) * BM + r].x);
+    f32x4 acc = f32x4{};
+    float l = 0.f;
+    if (m != -INFINITY) {
+      for (int p = 0; p < sp.parts; ++p) {
+        const float2 ml = wml[(u0 + p) * BM + r];
+        const float w = __builtin_amdgcn_exp2f(ml.x - m);
+        l = fmaf(w, ml.y, l);
+        const f32x4 o = *(const f32x4*)(a.ws + ((u0 + p) * BM + r) * D + 4 * c);
+        acc += w * o;
+      }
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (__bf16)(acc[e] * inv);
+    *(bf16x4*)((__bf16*)a.out + (int64_t)(q0 + r) * row_stride + (int64_t)head * D + 4 * c) = y;
+    if (c == 0 && a.lse != nullptr)
+      a.lse[(int64_t)(q0 + r) * a.H + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- tile-map export
 
-__global__ void __launch_bounds__(64) tile_map_kernel(const int32_t* q_cu, const int32_t* kv_cu,
-                                                      int R, int H, int block_m, int chunk, int32_t* out) {
+__global__ void __launch_bounds__(64) tile_map_kernel(const int32_t* q_cu, const int32_t* kv_cu, int R, int H,
+                                                      int block_m, int chunk, int slots, int max_kv, int32_t* out) {
   const int logical = block_to_logical(blockIdx.x, chunk);
-  int req, head, qt;
-  find_tile(q_cu, kv_cu, R, H, block_m, logical, req, head, qt);
+  const WorkItem w = work_item(q_cu, kv_cu, R, H, block_m, slots, max_kv, logical);
   if (threadIdx.x == 0) {
-    out[3 * (int64_t)blockIdx.x + 0] = req;
-    out[3 * (int64_t)blockIdx.x + 1] = req < 0 ? -1 : head;
-    out[3 * (int64_t)blockIdx.x + 2] = req < 0 ? -1 : qt;
+    const bool idle = w.req < 0;
+    int32_t* o = out + 5 * (int64_t)blockIdx.x;
+    o[0] = idle ? -1 : w.req;
+    o[1] = idle ? -1 : w.head;
+    o[2] = idle ? -1 : w.qt;
+    o[3] = idle ? -1 : w.part;
+    o[4] = idle ? -1 : w.parts;
   }
 }
 
@@ -775,24 +892,69 @@ constexpr int kChunk = 16;  // logical tiles kept together on one chiplet
 constexpr int kBf16VarlenWaves = 4;  // waves per work-group of the bf16 varlen kernel
 constexpr int kBf16VarlenQB = 1;     // 32-row query blocks per wave: 128 rows per work-group
 constexpr int kBf16VarlenBN = 64;    // keys per tile of the bf16 varlen kernel
+constexpr int kBf16VarlenBM = 32 * kBf16VarlenWaves * kBf16VarlenQB;
 constexpr int kF32Waves = 4;
+constexpr int kMaxDevices = 64;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The varlen launch for a dtype: query rows per work-group, threads, grid.
+template <int D>
+constexpr auto bf16_varlen_kernel() {
+  return &vl::attn_bf16_kernel<D, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>;
+}
+
+// Work-groups of the bf16 varlen kernel resident at once on the current
+// device (occupancy x compute units), 0 if it cannot be queried (no GPU).
+// Read once per device and head size, then cached.
+int bf16_varlen_slots(int D) {
+  static std::mutex mu;
+  static int cache[kMaxDevices][2];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int di = D == 128 ? 1 : 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev][di] > 0) return cache[dev][di];
+  int cus = 0, per_cu = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bf16_varlen_kernel<128>(), kBf16VarlenWaves * 64, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bf16_varlen_kernel<64>(), kBf16VarlenWaves * 64, 0);
+  if (e != hipSuccess || cus <= 0 || per_cu <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  cache[dev][di] = cus * per_cu;
+  return cache[dev][di];
+}
+
+// The varlen launch for a dtype: query rows per work-group, threads, grid,
+// and the slot count of the key split (0 = none).
 struct VarlenPlan {
   int block_m;
   int threads;
+  int slots;
   int64_t blocks;
 };
 
-inline VarlenPlan varlen_plan(bool f32, int64_t num_reqs, int64_t max_q, int64_t H) {
+inline VarlenPlan varlen_plan(bool f32, bool split, int64_t num_reqs, int64_t max_q, int64_t max_kv, int64_t H,
+                              int D) {
   VarlenPlan p;
   const int waves = f32 ? kF32Waves : kBf16VarlenWaves;
-  p.block_m = 32 * waves * (f32 ? 1 : kBf16VarlenQB);
+  p.block_m = f32 ? 32 * waves : kBf16VarlenBM;
   p.threads = 64 * waves;
-  p.blocks = (num_reqs == 0 || max_q == 0) ? 0 : vl::grid_blocks(num_reqs, max_q, H, p.block_m, kChunk);
+  // a split needs at least two key ranges of kMinSplitKeys keys
+  p.slots = (split && !f32 && max_kv / vl::kMinSplitKeys >= 2) ? bf16_varlen_slots(D) : 0;
+  p.blocks = (num_reqs == 0 || max_q == 0) ? 0 : vl::grid_blocks(num_reqs, max_q, H, p.block_m, kChunk, p.slots);
   return p;
+}
+
+// Bytes of partial results a split launch may write: per slot, BM rows of D
+// floats and BM (offset, sum) float pairs.
+inline int64_t split_workspace_bytes(int slots, int D) {
+  return (int64_t)slots * kBf16VarlenBM * ((int64_t)D * 4 + 8);
 }
 
 int launch_status() {
@@ -802,16 +964,20 @@ int launch_status() {
 template <bool kF32>
 int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_cu,
                   const int32_t* kv_cu, int32_t max_q, int32_t max_kv, int32_t num_reqs,
-                  int32_t H, int32_t D, float scale, void* out, float* lse, hipStream_t stream) {
+                  int32_t H, int32_t D, float scale, void* out, float* lse, bool split, void* workspace,
+                  int64_t workspace_bytes, hipStream_t stream) {
   if (num_reqs < 0 || max_q < 0 || max_kv < 0 || H < 1) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
   if (num_reqs == 0 || max_q == 0) return VL_OK;
   if (!q || !k || !v || !q_cu || !kv_cu || !out) return VL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
   if (!(scale == scale)) return VL_EINVAL;
-  const VarlenPlan plan = varlen_plan(kF32, num_reqs, max_q, H);
+  const VarlenPlan plan = varlen_plan(kF32, split, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
+  if (plan.slots > 0 &&
+      (!workspace || !aligned16(workspace) || workspace_bytes < split_workspace_bytes(plan.slots, D)))
+    return VL_EINVAL;
   vl::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -824,18 +990,30 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   a.H = H;
   a.chunk = kChunk;
   a.c = scale * vl::kLog2e;
+  a.slots = plan.slots;
+  a.max_kv = max_kv;
+  a.ws = (float*)workspace;
   (void)hipGetLastError();
   if (kF32) {
     if (D == 128)
       hipLaunchKernelGGL((vl::attn_f32_kernel<128, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
     else
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
-  } else {
+    return launch_status();
+  }
+  if (D == 128)
+    hipLaunchKernelGGL((vl::attn_bf16_kernel<128, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>),
+                       dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((vl::attn_bf16_kernel<64, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>),
+                       dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
+  if (plan.slots > 0) {
+    // one block per possible tail tile; blocks past the tail return at once
     if (D == 128)
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<128, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads), 0,
+      hipLaunchKernelGGL((vl::split_merge_kernel<128, kBf16VarlenBM>), dim3((unsigned)plan.slots), dim3(256), 0,
                          stream, a);
     else
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<64, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads), 0,
+      hipLaunchKernelGGL((vl::split_merge_kernel<64, kBf16VarlenBM>), dim3((unsigned)plan.slots), dim3(256), 0,
                          stream, a);
   }
   return launch_status();
@@ -892,7 +1070,22 @@ int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
                     const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
                     int32_t H, int32_t D, float scale, void* out, float* lse, vl_stream_t stream) {
   return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
-                              scale, out, lse, (hipStream_t)stream);
+                              scale, out, lse, false, nullptr, 0, (hipStream_t)stream);
+}
+
+int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
+                          const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
+                          int32_t H, int32_t D, float scale, void* out, float* lse, void* workspace,
+                          int64_t workspace_bytes, vl_stream_t stream) {
+  return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
+                              scale, out, lse, true, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int varlen_split_workspace_bytes(int32_t D, int64_t* bytes) {
+  if (!bytes) return VL_EINVAL;
+  if (D != 64 && D != 128) return VL_EUNSUPPORTED;
+  *bytes = split_workspace_bytes(bf16_varlen_slots(D), D);
+  return VL_OK;
 }
 
 int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
@@ -900,7 +1093,7 @@ int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
                         int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale,
                         float* out, float* lse, vl_stream_t stream) {
   return varlen_common<true>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
-                             scale, out, lse, (hipStream_t)stream);
+                             scale, out, lse, false, nullptr, 0, (hipStream_t)stream);
 }
 
 int block_local_attn_fwd(const void* q, const void* k, const void* v, int32_t B, int32_t n,
@@ -919,30 +1112,31 @@ int block_local_attn_fwd_f32(const float* q, const float* k, const float* v, int
                                   lse, (hipStream_t)stream);
 }
 
-int varlen_launch_shape(int32_t max_q, int32_t num_reqs, int32_t H, int32_t D, int dtype_f32,
-                        int32_t* block_m, int32_t* chunk, int64_t* blocks) {
-  if (max_q < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
+int varlen_launch_shape(int32_t max_q, int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, int dtype_f32,
+                        int split, int32_t* block_m, int32_t* chunk, int64_t* blocks, int32_t* slots) {
+  if (max_q < 0 || max_kv < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
-  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, num_reqs, max_q, H);
+  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, split != 0, num_reqs, max_q, max_kv, H, D);
   if (block_m) *block_m = plan.block_m;
   if (chunk) *chunk = kChunk;
   if (blocks) *blocks = plan.blocks;
+  if (slots) *slots = plan.slots;
   return VL_OK;
 }
 
-int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, int32_t max_q,
-                    int32_t num_reqs, int32_t H, int32_t D, int dtype_f32, int32_t* triples_out,
+int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv,
+                    int32_t num_reqs, int32_t H, int32_t D, int dtype_f32, int split, int32_t* items_out,
                     int64_t max_blocks, vl_stream_t stream) {
-  int64_t G = 0;
-  int32_t bm = 0;
-  const int rc = varlen_launch_shape(max_q, num_reqs, H, D, dtype_f32, &bm, nullptr, &G);
-  if (rc != VL_OK) return rc;
+  if (max_q < 0 || max_kv < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
+  if (D != 64 && D != 128) return VL_EUNSUPPORTED;
+  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, split != 0, num_reqs, max_q, max_kv, H, D);
+  const int64_t G = plan.blocks;
   if (G == 0) return VL_OK;
-  if (!q_cu_seqlens || !kv_cu_seqlens || !triples_out || max_blocks < G) return VL_EINVAL;
+  if (!q_cu_seqlens || !kv_cu_seqlens || !items_out || max_blocks < G) return VL_EINVAL;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
   (void)hipGetLastError();
   hipLaunchKernelGGL(vl::tile_map_kernel, dim3((unsigned)G), dim3(64), 0, (hipStream_t)stream, q_cu_seqlens,
-                     kv_cu_seqlens, num_reqs, H, bm, kChunk, triples_out);
+                     kv_cu_seqlens, num_reqs, H, plan.block_m, kChunk, plan.slots, max_kv, items_out);
   return launch_status();
 }
 

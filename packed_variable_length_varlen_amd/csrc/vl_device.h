@@ -26,6 +26,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kXcds = 8;          // chiplets; block ids are dealt to them round-robin
 constexpr int kLptMaxReqs = 64;   // longest-first request order up to this many requests
+constexpr int kMaxSplit = 16;       // key ranges a tile of the last round is cut into, at most
+constexpr int kMinSplitKeys = 256;  // and no more ranges than max_kv / this
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -133,11 +135,91 @@ __device__ __forceinline__ void find_tile(const int32_t* __restrict__ q_cu,
   }
 }
 
-// Host-side launch size: upper bound on the tile count, rounded up to whole
-// groups of (chiplets x chunk) so the block -> tile map is a bijection.
+// Number of (request, head, q-tile) tiles.  Executed by a whole wave; the
+// result is wave-uniform.
+__device__ __forceinline__ int total_tiles(const int32_t* __restrict__ q_cu, int R, int H, int block_m) {
+  int sum = 0;
+  for (int r0 = 0; r0 < R; r0 += 64) {
+    const int r = r0 + lane_id();
+    int cnt = r < R ? ((q_cu[r + 1] - q_cu[r] + block_m - 1) / block_m) * H : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    sum += cnt;
+  }
+  return sum;
+}
+
+// Key split of the last, partial round of a launch with `slots` resident
+// work-groups.  Logical tiles [0, full) run whole.  When the remaining
+// tail = T - full tiles would leave at least half of the slots idle, each of
+// them is cut into `parts` key ranges (at most kMaxSplit, and at most
+// max_kv / kMinSplitKeys), run as tail * parts separate work items whose
+// partial results a second kernel merges.  parts == 1 means no split
+// (full == T).  slots <= 0 turns the split off.
+struct SplitPlan {
+  int full;
+  int tail;
+  int parts;
+};
+__host__ __device__ inline SplitPlan split_plan(int T, int slots, int max_kv) {
+  SplitPlan p{T, 0, 1};
+  if (slots <= 0 || T <= 0) return p;
+  const int full = T >= slots ? (T / slots) * slots : 0;
+  const int tail = T - full;
+  if (tail == 0) return p;
+  int parts = slots / tail;
+  if (parts > kMaxSplit) parts = kMaxSplit;
+  if (parts > max_kv / kMinSplitKeys) parts = max_kv / kMinSplitKeys;
+  if (parts < 2) return p;
+  p.full = full;
+  p.tail = tail;
+  p.parts = parts;
+  return p;
+}
+
+// Key tiles [lo, hi) of part `part` of `parts` of a key range of nkt tiles.
+__host__ __device__ inline void split_range(int nkt, int part, int parts, int& lo, int& hi) {
+  lo = (int)((int64_t)part * nkt / parts);
+  hi = (int)((int64_t)(part + 1) * nkt / parts);
+}
+
+// One unit of work of the varlen launch: a whole tile (part 0 of 1, unit -1)
+// or key range `part` of `parts` of a tile of the last round (unit = index
+// of its partial-result slot).  req = -1: nothing to do.
+struct WorkItem {
+  int req, head, qt, part, parts, unit;
+};
+
+__device__ __forceinline__ WorkItem work_item(const int32_t* __restrict__ q_cu, const int32_t* __restrict__ kv_cu,
+                                              int R, int H, int block_m, int slots, int max_kv, int logical) {
+  WorkItem w{-1, -1, -1, -1, -1, -1};
+  int tile = logical;
+  int part = 0, parts = 1, unit = -1;
+  if (slots > 0) {
+    const SplitPlan sp = split_plan(total_tiles(q_cu, R, H, block_m), slots, max_kv);
+    if (sp.parts > 1 && logical >= sp.full) {
+      const int u = logical - sp.full;
+      if (u >= sp.tail * sp.parts) return w;
+      tile = sp.full + u / sp.parts;
+      part = u % sp.parts;
+      parts = sp.parts;
+      unit = u;
+    }
+  }
+  find_tile(q_cu, kv_cu, R, H, block_m, tile, w.req, w.head, w.qt);
+  if (w.req < 0) return w;
+  w.part = part;
+  w.parts = parts;
+  w.unit = unit;
+  return w;
+}
+
+// Host-side launch size: upper bound on the tile count (plus one round of
+// slots for the split work items), rounded up to whole groups of
+// (chiplets x chunk) so the block -> logical map is a bijection.
 inline int64_t grid_blocks(int64_t num_reqs, int64_t max_q, int64_t H, int64_t block_m,
-                           int64_t chunk) {
-  const int64_t upper = num_reqs * H * ((max_q + block_m - 1) / block_m);
+                           int64_t chunk, int64_t slots = 0) {
+  const int64_t upper = num_reqs * H * ((max_q + block_m - 1) / block_m) + (slots > 0 ? slots : 0);
   const int64_t group = kXcds * chunk;
   return ((upper + group - 1) / group) * group;
 }

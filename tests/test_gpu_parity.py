@@ -128,9 +128,10 @@ def test_joint_pack_with_offsets_bitexact():
 # ------------------------------------------------------------------ tile schedule
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("case", ["lpt", "ties", "index_order", "empty", "qkv_differ"])
-def test_tile_map_bitexact(case):
-    log(f"[tile_map] {case}")
+def test_tile_map_bitexact(case, split):
+    log(f"[tile_map] {case} split={split}")
     rng = np.random.default_rng(3)
     if case == "lpt":
         ql = [17, 64, 129, 4096, 300, 1]
@@ -151,18 +152,26 @@ def test_tile_map_bitexact(case):
     q_cu = oracle.cu_seqlens_from_lengths(ql)
     kv_cu = oracle.cu_seqlens_from_lengths(kl)
     max_q = max(max(ql), 1)
-    bm, chunk, G = vl.varlen_launch_shape(max_q, len(ql), H, D)
+    max_kv = int(max(kl))
+    bm, chunk, G, slots = vl.varlen_launch_shape(max_q, len(ql), H, D, max_kv=max_kv, split=split)
+    if split and max_kv // oracle.MIN_SPLIT_KEYS >= 2:
+        assert slots >= 256, "a split launch sizes itself by the device's resident work-groups"
+    else:
+        assert slots == 0, "no split without the flag or with keys too short to cut"
     got = vl.varlen_tile_map(torch.from_numpy(q_cu.astype(np.int32)).to(DEV),
-                             torch.from_numpy(kv_cu.astype(np.int32)).to(DEV), max_q, H, D).cpu().numpy()
-    ref = oracle.block_schedule(q_cu, kv_cu, H, bm, max_q, chunk)
+                             torch.from_numpy(kv_cu.astype(np.int32)).to(DEV), max_q, H, D,
+                             max_kv=max_kv, split=split).cpu().numpy()
+    ref = oracle.block_schedule(q_cu, kv_cu, H, bm, max_q, chunk, slots=slots, max_kv=max_kv)
     assert got.shape == ref.shape
     assert np.array_equal(got, ref.astype(np.int32))
+    if split and case == "lpt":
+        assert (got[:, 4] > 1).any(), "this case has a tail to split"
 
 
 # ------------------------------------------------------------------ varlen attention
 
 
-def _run_varlen(q, k, v, q_cu, kv_cu, scale, f32, max_q=None, max_kv=None):
+def _run_varlen(q, k, v, q_cu, kv_cu, scale, f32, max_q=None, max_kv=None, split=False):
     ql = np.diff(q_cu)
     kl = np.diff(kv_cu)
     max_q = int(ql.max()) if max_q is None and ql.size else (max_q or 0)
@@ -171,7 +180,7 @@ def _run_varlen(q, k, v, q_cu, kv_cu, scale, f32, max_q=None, max_kv=None):
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
     full, out = canary_out(tuple(q.shape), dtype)
     lse_full, lse = canary_out((q.shape[0], q.shape[1]), torch.float32)
-    fn = vl.varlen_attn_fwd_f32 if f32 else vl.varlen_attn_fwd
+    fn = vl.varlen_attn_fwd_f32 if f32 else (vl.varlen_attn_fwd_split if split else vl.varlen_attn_fwd)
     fn(qd, kd, vd, torch.from_numpy(np.asarray(q_cu, dtype=np.int32)).to(DEV),
        torch.from_numpy(np.asarray(kv_cu, dtype=np.int32)).to(DEV), max_q, max_kv, scale, out=out, lse=lse)
     torch.cuda.synchronize()
@@ -263,6 +272,92 @@ def test_varlen_invariants_bitwise():
         assert torch.equal(op[int(cup[i]):int(cup[i + 1])], out[int(cu[r]):int(cu[r + 1])])
 
 
+# ------------------------------------------------------------------ key split of the last round
+
+
+def _split_parts(ql, kl, H, D):
+    """parts of the split plan the device would use for this batch."""
+    bm, _, _, slots = vl.varlen_launch_shape(max(ql), len(ql), H, D, max_kv=max(kl), split=True)
+    T = len(oracle.tile_order(oracle.cu_seqlens_from_lengths(ql), oracle.cu_seqlens_from_lengths(kl), H, bm))
+    return oracle.split_plan(T, slots, max(kl)), slots
+
+
+SPLIT_CASES = [
+    # one round only: every tile is cut
+    ("one_request", [3000], None, 2, 128),
+    # ragged q tiles, a kv length with empty key ranges, a request with no keys
+    ("ragged_empty_parts", [300, 130, 1, 2000], [5000, 70, 0, 2000], 3, 128),
+    ("d64_q_ne_kv", [77, 640, 129], [1500, 9, 1300], 2, 64),
+]
+
+
+@pytest.mark.parametrize("name,ql,kl,H,D", SPLIT_CASES)
+def test_varlen_split_vs_oracle(name, ql, kl, H, D):
+    kl = ql if kl is None else kl
+    (full, tail, parts), slots = _split_parts(ql, kl, H, D)
+    log(f"[split] {name}: slots {slots} full {full} tail {tail} parts {parts}")
+    assert parts >= 2, "the case must exercise the split"
+    q, k, v = wl.random_varlen_case(41, ql, H, D, torch.bfloat16, kl)
+    q_cu = oracle.cu_seqlens_from_lengths(ql)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    scale = wl.softmax_scale(D)
+    out, lse = _run_varlen(q, k, v, q_cu, kv_cu, scale, False, split=True)
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), q_cu, kv_cu, scale)
+    check_close(to64(out), ro, False, name)
+    check_lse(to64(lse), rl, False, name)
+    # against the unsplit launch: the same math up to fp32 summation order
+    o1, l1 = _run_varlen(q, k, v, q_cu, kv_cu, scale, False)
+    assert (o1.float() - out.float()).abs().max().item() <= 2 ** -7
+    fin = torch.isfinite(l1)
+    assert torch.equal(fin, torch.isfinite(lse))
+    assert (l1[fin] - lse[fin]).abs().max().item() <= 1e-4
+
+
+def test_varlen_split_after_full_rounds():
+    """More tiles than slots: the whole rounds run unsplit, the tail is cut.
+    Compared with the oracle on every row of the tail tiles and a sample of
+    the rest."""
+    H, D = 1, 64
+    _, _, _, slots = vl.varlen_launch_shape(128, 1, H, D, max_kv=1024, split=True)
+    R = slots + 5
+    ql = [128] * R
+    kl = [1024] * R
+    (full, tail, parts), _ = _split_parts(ql, kl, H, D)
+    log(f"[split] {R} requests: slots {slots} full {full} tail {tail} parts {parts}")
+    assert (full, tail, parts) == (slots, 5, 4)
+    q, k, v = wl.random_varlen_case(43, ql, H, D, torch.bfloat16, kl)
+    q_cu = oracle.cu_seqlens_from_lengths(ql)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    scale = wl.softmax_scale(D)
+    out, lse = _run_varlen(q, k, v, q_cu, kv_cu, scale, False, split=True)
+    # tiles are visited in request order here (more than 64 requests): the
+    # tail tiles are the last five requests
+    tail_rows = np.arange(int(q_cu[R - 5]), int(q_cu[R]))
+    rows = np.union1d(tail_rows, np.random.default_rng(1).choice(int(q_cu[R - 5]), 300, replace=False))
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), q_cu, kv_cu, scale, rows=rows)
+    check_close(to64(out)[rows], ro, False, "split tail")
+    check_lse(to64(lse)[rows], rl, False, "split tail")
+
+
+def test_varlen_split_workspace_checked():
+    """A split launch refuses a missing or short workspace before launching."""
+    ql = [3000]
+    q, k, v = wl.random_varlen_case(47, ql, 1, 128, torch.bfloat16)
+    cu = torch.tensor([0, 3000], dtype=torch.int32, device=DEV)
+    need = vl.varlen_split_workspace_bytes(128)
+    assert need > 0
+    short = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(vl.VarlenError):
+        vl.varlen_attn_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), cu, cu, 3000, 3000, workspace=short)
+    # no split possible (max_kv < 512): the workspace is not needed
+    small = [100]
+    q2, k2, v2 = wl.random_varlen_case(48, small, 1, 128, torch.bfloat16)
+    cu2 = torch.tensor([0, 100], dtype=torch.int32, device=DEV)
+    o_split = vl.varlen_attn_fwd_split(q2.to(DEV), k2.to(DEV), v2.to(DEV), cu2, cu2, 100, 100, workspace=short)
+    o_plain = vl.varlen_attn_fwd(q2.to(DEV), k2.to(DEV), v2.to(DEV), cu2, cu2, 100, 100)
+    assert torch.equal(o_split, o_plain)
+
+
 def _pipeline(inp):
     """The hot path on the GPU: boundaries from the text mask and grids, joint
     pack of q/k/v, varlen attention, unpack of the outputs."""
@@ -279,7 +374,8 @@ def _pipeline(inp):
         packed.append(dst)
     q, k, v = packed
     max_len = inp.max_len
-    fn = vl.varlen_attn_fwd_f32 if inp.dtype == torch.float32 else vl.varlen_attn_fwd
+    # bf16 runs the launch the benchmark times (key split of the last round)
+    fn = vl.varlen_attn_fwd_f32 if inp.dtype == torch.float32 else vl.varlen_attn_fwd_split
     out, lse = fn(q, k, v, cu_j, cu_j, max_len, max_len, inp.scale, return_lse=True)
     out_txt = torch.empty_like(inp.q_text, device=DEV)
     out_img = torch.empty_like(inp.q_img, device=DEV)

@@ -77,14 +77,22 @@ def test_bad_scalars_rejected_before_launch(lib):
     assert lib.cu_seqlens_from_lengths(p, -1, p, None) == VL_EINVAL
     assert lib.joint_cu_seqlens(p, -1, p, 2, p, p, p, p, None) == VL_EINVAL
     # tile map: output too small
-    assert lib.varlen_tile_map(p, p, 300, 4, 2, 128, 0, p, 1, None) == VL_EINVAL
+    assert lib.varlen_tile_map(p, p, 300, 300, 4, 2, 128, 0, 0, p, 1, None) == VL_EINVAL
+    # split entry point: same scalar checks as the plain one
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 96, 0.1, p, None, p, 0, None) == VL_EUNSUPPORTED
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, -1, 8, 1, 2, 64, 0.1, p, None, p, 0, None) == VL_EINVAL
+    assert lib.varlen_split_workspace_bytes(96, p) == VL_EUNSUPPORTED
+    assert lib.varlen_split_workspace_bytes(64, None) == VL_EINVAL
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("max_q,R,H,D", [(210, 3, 2, 64), (16640, 1, 24, 128), (16640, 4, 24, 128),
                                          (33024, 4, 24, 128), (1, 100, 1, 64), (0, 3, 2, 64)])
-def test_launch_shape_matches_schedule_spec(lib, max_q, R, H, D):
-    bm, chunk, G = vl.varlen_launch_shape(max_q, R, H, D)
-    expect = oracle.grid_blocks(R, max_q, H, bm, chunk) if max_q > 0 and R > 0 else 0
+def test_launch_shape_matches_schedule_spec(lib, max_q, R, H, D, split):
+    bm, chunk, G, slots = vl.varlen_launch_shape(max_q, R, H, D, max_kv=max_q, split=split)
+    if not split:
+        assert slots == 0
+    expect = oracle.grid_blocks(R, max_q, H, bm, chunk, slots=slots) if max_q > 0 and R > 0 else 0
     assert G == expect
     assert G % (8 * chunk) == 0
 

@@ -139,14 +139,70 @@ def test_tile_order_counts_uniqueness_and_order():
     assert [t[0] for t in t3] == [0, 1, 2]
 
 
+def test_split_plan_worked_values():
+    """Hand-computed plans: one joint 16,640-token request with 24 heads has
+    130 * 24 = 3120 tiles; on 512 slots six rounds run whole and the 48 left
+    are cut into min(16, 512 // 48, 16640 // 256) = 10 key ranges."""
+    assert oracle.split_plan(3120, 512, 16640) == (3072, 48, 10)
+    # a whole number of rounds: nothing to cut
+    assert oracle.split_plan(3072, 512, 16640) == (3072, 0, 1)
+    # the tail fills more than half of the slots: nothing to cut
+    assert oracle.split_plan(512 + 300, 512, 16640) == (812, 0, 1)
+    # one round only: every tile is cut, capped at MAX_SPLIT
+    assert oracle.split_plan(20, 512, 1 << 20) == (0, 20, 16)
+    # short keys cap the ranges: 700 keys -> 2 ranges; 511 keys -> none
+    assert oracle.split_plan(20, 512, 700) == (0, 20, 2)
+    assert oracle.split_plan(20, 512, 511) == (20, 0, 1)
+    # no slots (split off) or no tiles
+    assert oracle.split_plan(20, 0, 1 << 20) == (20, 0, 1)
+    assert oracle.split_plan(0, 512, 1 << 20) == (0, 0, 1)
+
+
+def test_split_ranges_tile_the_keys():
+    for nkt in (0, 1, 2, 5, 16, 17, 260):
+        for parts in (2, 3, 10, 16):
+            spans = [oracle.split_range(nkt, p, parts) for p in range(parts)]
+            assert spans[0][0] == 0 and spans[-1][1] == nkt
+            assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
+            assert all(lo <= hi for lo, hi in spans)
+            sizes = [hi - lo for lo, hi in spans]
+            assert max(sizes) - min(sizes) <= 1
+
+
+def test_block_schedule_with_split_covers_every_tile_once():
+    q_cu = oracle.cu_seqlens_from_lengths([17, 64, 129, 300, 2000])
+    kv_cu = oracle.cu_seqlens_from_lengths([17, 640, 129, 3000, 2000])
+    H, bm, chunk = 2, 128, 4
+    tiles = oracle.tile_order(q_cu, kv_cu, H, bm)
+    for slots in (8, 12, 40, 512):
+        full, tail, parts = oracle.split_plan(len(tiles), slots, 3000)
+        sched = oracle.block_schedule(q_cu, kv_cu, H, bm, 2000, chunk, slots=slots, max_kv=3000)
+        G = oracle.grid_blocks(5, 2000, H, bm, chunk, slots=slots)
+        assert sched.shape == (G, 5)
+        used = [tuple(x) for x in sched if x[0] >= 0]
+        assert len(used) == full + tail * parts <= len(tiles) + slots
+        # every tile: whole exactly once, or each of its parts exactly once
+        seen = {}
+        for r, h, qt, p, n in used:
+            seen.setdefault((r, h, qt), []).append((p, n))
+        assert sorted(seen) == sorted(tiles)
+        for t, ps in seen.items():
+            n = ps[0][1]
+            assert sorted(ps) == [(p, n) for p in range(n)]
+        split_tiles = [t for t, ps in seen.items() if ps[0][1] > 1]
+        assert len(split_tiles) == tail
+        assert set(split_tiles) == set(tiles[full:])
+
+
 def test_block_schedule_is_a_bijection_onto_tiles():
     q_cu = oracle.cu_seqlens_from_lengths([17, 64, 129, 300])
     for chunk in (1, 4, 16):
         sched = oracle.block_schedule(q_cu, q_cu, 2, 32, 300, chunk)
         tiles = oracle.tile_order(q_cu, q_cu, 2, 32)
         G = oracle.grid_blocks(4, 300, 2, 32, chunk)
-        assert sched.shape == (G, 3) and G % (8 * chunk) == 0
-        used = [tuple(x) for x in sched if x[0] >= 0]
+        assert sched.shape == (G, 5) and G % (8 * chunk) == 0
+        assert (sched[sched[:, 0] >= 0][:, 3:] == (0, 1)).all()
+        used = [tuple(x[:3]) for x in sched if x[0] >= 0]
         assert sorted(used) == sorted(tiles)
         assert len(used) == len(tiles)
         # the logical map itself is a permutation of [0, G)
