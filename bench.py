@@ -2,10 +2,11 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   1. boundaries (cu_seqlens) from the real text mask and the image grids,
-  2. joint text+image pack of Q, K and V into flat [T, H, D],
+  2. joint text+image pack of Q, K and V into flat [T, H, D] (one launch),
   3. flat varlen attention (bf16 MFMA, fp32 accumulation; the last, partial
      round of work-groups cut along the keys and merged),
-  4. unpack of the output back to the per-request text / image layout,
+  4. unpack of the output back to the per-request text / image layout (one
+     launch),
   5. block-local attention of the vocoder-DiT shape (n=2003, 24-frame blocks,
      H=16, D=64) for each of the four window types (own block, one back,
      one ahead, both).
@@ -180,6 +181,13 @@ def main():
     bq, bk, bv = bl.q.to(dev), bl.k.to(dev), bl.v.to(dev)
     bouts = [torch.empty_like(bq) for _ in bl_spec.windows]
 
+    # the joint pack of Q, K, V (text and image pieces: six copies) and the
+    # unpack of the output (two copies), one launch each
+    pack_items = []
+    for (txt, img), dst in zip(slabs, packed):
+        pack_items += [(txt, cu_t, dst, cu_j[:-1]), (img, cu_i, dst, img_dst)]
+    unpack_items = [(out, cu_t, out_txt, cu_j[:-1]), (out, cu_i, out_img, img_dst)]
+
     stream = torch.cuda.current_stream()
     ev = {"attn": [], "pack": [], "unpack": [], "blocal": []}
 
@@ -193,15 +201,12 @@ def main():
     def step(record: bool):
         vl.joint_cu_seqlens(mask_d, hw_d, outs=(cu_j, cu_t, cu_i, img_dst))
         e0 = mark(record)
-        for (txt, img), dst in zip(slabs, packed):
-            vl.pack_by_cu_seqlens(txt, cu_t, dst, dst_row_offsets=cu_j[:-1])
-            vl.pack_by_cu_seqlens(img, cu_i, dst, dst_row_offsets=img_dst)
+        vl.pack_by_cu_seqlens_batched(pack_items)
         e1 = mark(record)
         vl.varlen_attn_fwd_split(packed[0], packed[1], packed[2], cu_j, cu_j, max_len, max_len, inp.scale,
                                  out=out, workspace=workspace)
         e2 = mark(record)
-        vl.unpack_by_cu_seqlens(out, cu_t, out_txt, src_row_offsets=cu_j[:-1])
-        vl.unpack_by_cu_seqlens(out, cu_i, out_img, src_row_offsets=img_dst)
+        vl.unpack_by_cu_seqlens_batched(unpack_items)
         e3 = mark(record)
         for (lb, la), o in zip(bl_spec.windows, bouts):
             vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o)

@@ -86,6 +86,32 @@ int unpack_by_cu_seqlens(const void* src_flat, const int32_t* src_row_offsets,
                          const int32_t* cu_seqlens, int32_t num_reqs, int64_t row_bytes,
                          void* dst_padded, int64_t max_len, int zero_fill, vl_stream_t stream);
 
+/* pack_by_cu_seqlens_batched / unpack_by_cu_seqlens_batched: up to 8 pack
+ *   (or unpack) calls in one launch, e.g. the text and image pieces of Q, K
+ *   and V of a joint batch.  descs: HOST array of `count` descriptors (read
+ *   during the call only); descriptor i means exactly
+ *     pack_by_cu_seqlens(src, max_len, cu_seqlens, num_reqs, row_bytes, dst,
+ *                        row_offsets)
+ *   resp. unpack_by_cu_seqlens(src, row_offsets, cu_seqlens, num_reqs,
+ *                              row_bytes, dst, max_len, zero_fill)
+ *   with the same argument rules (zero_fill is ignored by pack).  The copies
+ *   run in no particular order, so no destination may overlap another copy's
+ *   source or destination.  0 <= count <= 8, else VL_EINVAL.  When every copy
+ *   moves 16-byte vectors it is one kernel launch, otherwise one per copy.
+ */
+typedef struct {
+  const void* src;
+  void* dst;
+  const int32_t* cu_seqlens;
+  const int32_t* row_offsets;
+  int64_t max_len;
+  int64_t row_bytes;
+  int32_t num_reqs;
+  int32_t zero_fill;
+} vl_copy_desc;
+int pack_by_cu_seqlens_batched(const vl_copy_desc* descs, int32_t count, vl_stream_t stream);
+int unpack_by_cu_seqlens_batched(const vl_copy_desc* descs, int32_t count, vl_stream_t stream);
+
 /* unpack_cfg_combine: per-request classifier-free-guidance combine fused into
  *   the unpack (vLLM-Omni PR #4024, "CFG behavior": the combine
  *   negative + true_cfg_scale * (positive - negative) is applied after the

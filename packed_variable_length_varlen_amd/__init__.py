@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "load_library", "lib_path", "cu_seqlens_from_lengths", "joint_cu_seqlens",
-    "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "varlen_attn_fwd", "varlen_attn_fwd_split",
+    "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "pack_by_cu_seqlens_batched",
+    "unpack_by_cu_seqlens_batched", "varlen_attn_fwd", "varlen_attn_fwd_split",
     "varlen_split_workspace_bytes", "varlen_attn_fwd_f32",
     "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
     "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError",
@@ -56,12 +57,23 @@ _SIGNATURES = {
     "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _c_i64, _vp],
                         _c_int),
     "mixfusion_chunk_plan": ([_vp, _c_i32, _c_i64, _c_i64, _vp, _vp], _c_int),
+    "pack_by_cu_seqlens_batched": ([_vp, _c_i32, _vp], _c_int),
+    "unpack_by_cu_seqlens_batched": ([_vp, _c_i32, _vp], _c_int),
     "unpack_cfg_combine": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i64, _vp, _c_i64, _c_int, _vp], _c_int),
 }
 
 
 class VarlenError(RuntimeError):
     pass
+
+
+class _CopyDesc(ctypes.Structure):
+    """vl_copy_desc of include/varlen.h."""
+    _fields_ = [("src", _vp), ("dst", _vp), ("cu_seqlens", _vp), ("row_offsets", _vp),
+                ("max_len", _c_i64), ("row_bytes", _c_i64), ("num_reqs", _c_i32), ("zero_fill", _c_i32)]
+
+
+MAX_BATCH = 8  # copies per batched pack / unpack call
 
 
 def lib_path() -> str:
@@ -100,6 +112,14 @@ def _stream(stream) -> int:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _row_bytes(flat: torch.Tensor) -> int:
+    """Bytes of one row (all dims but the first); valid for an empty tensor too."""
+    n = 1
+    for x in flat.shape[1:]:
+        n *= int(x)
+    return n * flat.element_size()
 
 
 def _gpu(t: torch.Tensor, name: str, dtype=None, contiguous: bool = True):
@@ -162,7 +182,7 @@ def pack_by_cu_seqlens(src_padded: torch.Tensor, cu_seqlens: torch.Tensor, dst_f
     R = cu_seqlens.numel() - 1
     if src_padded.shape[0] != R or tuple(src_padded.shape[2:]) != tuple(dst_flat.shape[1:]):
         raise VarlenError("src_padded must be [num_reqs, max_len, *row] and dst_flat [T, *row]")
-    row_bytes = dst_flat[0].numel() * dst_flat.element_size() if dst_flat.dim() > 1 else dst_flat.element_size()
+    row_bytes = _row_bytes(dst_flat)
     _check(load_library().pack_by_cu_seqlens(_ptr(src_padded), src_padded.shape[1], _ptr(cu_seqlens), R,
                                              row_bytes, _ptr(dst_flat), _ptr(dst_row_offsets),
                                              _stream(stream)), "pack_by_cu_seqlens")
@@ -181,12 +201,56 @@ def unpack_by_cu_seqlens(src_flat: torch.Tensor, cu_seqlens: torch.Tensor, dst_p
     R = cu_seqlens.numel() - 1
     if dst_padded.shape[0] != R or tuple(dst_padded.shape[2:]) != tuple(src_flat.shape[1:]):
         raise VarlenError("dst_padded must be [num_reqs, max_len, *row] and src_flat [T, *row]")
-    row_bytes = src_flat[0].numel() * src_flat.element_size() if src_flat.dim() > 1 else src_flat.element_size()
+    row_bytes = _row_bytes(src_flat)
     _check(load_library().unpack_by_cu_seqlens(_ptr(src_flat), _ptr(src_row_offsets), _ptr(cu_seqlens), R,
                                                row_bytes, _ptr(dst_padded), dst_padded.shape[1],
                                                1 if zero_fill else 0, _stream(stream)),
            "unpack_by_cu_seqlens")
     return dst_padded
+
+
+def pack_by_cu_seqlens_batched(items, stream=None):
+    """Several pack_by_cu_seqlens calls in one launch.  items: up to 8 tuples
+    (src_padded, cu_seqlens, dst_flat, dst_row_offsets or None); destinations
+    must not overlap each other or any source."""
+    items = list(items)
+    if len(items) > MAX_BATCH:
+        raise VarlenError(f"at most {MAX_BATCH} copies per batched call")
+    descs = (_CopyDesc * max(len(items), 1))()
+    for i, (src, cu, dst, offs) in enumerate(items):
+        _gpu(src, "src_padded")
+        _gpu(dst, "dst_flat", src.dtype)
+        _gpu(cu, "cu_seqlens", torch.int32)
+        if offs is not None:
+            _gpu(offs, "dst_row_offsets", torch.int32)
+        R = cu.numel() - 1
+        if src.shape[0] != R or tuple(src.shape[2:]) != tuple(dst.shape[1:]):
+            raise VarlenError("src_padded must be [num_reqs, max_len, *row] and dst_flat [T, *row]")
+        descs[i] = _CopyDesc(_ptr(src), _ptr(dst), _ptr(cu), _ptr(offs), src.shape[1], _row_bytes(dst), R, 0)
+    _check(load_library().pack_by_cu_seqlens_batched(ctypes.cast(descs, _vp), len(items), _stream(stream)),
+           "pack_by_cu_seqlens_batched")
+
+
+def unpack_by_cu_seqlens_batched(items, zero_fill: bool = True, stream=None):
+    """Several unpack_by_cu_seqlens calls in one launch.  items: up to 8 tuples
+    (src_flat, cu_seqlens, dst_padded, src_row_offsets or None)."""
+    items = list(items)
+    if len(items) > MAX_BATCH:
+        raise VarlenError(f"at most {MAX_BATCH} copies per batched call")
+    descs = (_CopyDesc * max(len(items), 1))()
+    for i, (src, cu, dst, offs) in enumerate(items):
+        _gpu(src, "src_flat")
+        _gpu(dst, "dst_padded", src.dtype)
+        _gpu(cu, "cu_seqlens", torch.int32)
+        if offs is not None:
+            _gpu(offs, "src_row_offsets", torch.int32)
+        R = cu.numel() - 1
+        if dst.shape[0] != R or tuple(dst.shape[2:]) != tuple(src.shape[1:]):
+            raise VarlenError("dst_padded must be [num_reqs, max_len, *row] and src_flat [T, *row]")
+        descs[i] = _CopyDesc(_ptr(src), _ptr(dst), _ptr(cu), _ptr(offs), dst.shape[1], _row_bytes(src), R,
+                             1 if zero_fill else 0)
+    _check(load_library().unpack_by_cu_seqlens_batched(ctypes.cast(descs, _vp), len(items), _stream(stream)),
+           "unpack_by_cu_seqlens_batched")
 
 
 def unpack_cfg_combine(src_flat: torch.Tensor, seg_cu: torch.Tensor, pos_rows: torch.Tensor,
@@ -203,7 +267,7 @@ def unpack_cfg_combine(src_flat: torch.Tensor, seg_cu: torch.Tensor, pos_rows: t
         raise VarlenError("seg_cu [R+1], pos_rows / neg_rows / scale [R] and dst_padded [R, ...] must agree")
     if tuple(dst_padded.shape[2:]) != tuple(src_flat.shape[1:]):
         raise VarlenError("dst_padded must be [R, max_len, *row] and src_flat [T, *row]")
-    row_elems = src_flat[0].numel() if src_flat.dim() > 1 else 1
+    row_elems = _row_bytes(src_flat) // src_flat.element_size()
     _check(load_library().unpack_cfg_combine(_ptr(src_flat), _ptr(seg_cu), _ptr(pos_rows), _ptr(neg_rows),
                                              _ptr(scale), R, row_elems, _ptr(dst_padded), dst_padded.shape[1],
                                              1 if zero_fill else 0, _stream(stream)), "unpack_cfg_combine")

@@ -274,7 +274,7 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
 // co-limiter at 32 rows per wave); such a wave takes one SIMD's whole register
 // file, and 32-key tiles keep its two score buffers within it.
 template <int D, int WAVES, int QB, int BN, bool kBlockLocal>
-__global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 2 : 1)) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf16_kernel(AttnArgs a) {
   using G = Bf16Geo<D, WAVES, BN>;
   constexpr int BM = 32 * QB * WAVES;
   // Two separate buffers (not one indexed array) so that the compiler sees

@@ -12,7 +12,7 @@
 namespace vl {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 8;  // independent 16-byte loads in flight per thread
+constexpr int kCopyUnroll = 4;  // 16-byte loads in flight per thread (4 streams HBM best; 8 is slower)
 constexpr int kUnitsPerBlock = kCopyThreads * kCopyUnroll;
 
 // Request r = blockIdx.y copies units [0, len_r*row_units) of its slab in
@@ -50,6 +50,55 @@ __global__ void __launch_bounds__(kCopyThreads) copy_segments_kernel(
   for (int i = 0; i < kCopyUnroll; ++i) {
     const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
     if (u < span_units) __builtin_nontemporal_store(buf[i], d + u);
+  }
+}
+
+// Up to kMaxBatch pack (or unpack) copies in one launch, 16-byte units.
+// Blocks are numbered flat: copy i owns blocks [b0[i], b0[i+1]), bx[i] per
+// request; block b0[i] + r*bx[i] + j streams units [j, j+1) * kUnitsPerBlock
+// of request r.  The descriptors travel by value in the kernel arguments.
+constexpr int kMaxBatch = 8;
+struct CopyBatch {
+  const u32x4* src[kMaxBatch];
+  u32x4* dst[kMaxBatch];
+  const int32_t* cu[kMaxBatch];
+  const int32_t* offsets[kMaxBatch];
+  int64_t row_units[kMaxBatch];
+  int64_t slab_rows[kMaxBatch];
+  int64_t bx[kMaxBatch];
+  int64_t b0[kMaxBatch + 1];
+  int zero_tail[kMaxBatch];
+  int count;
+};
+
+template <bool kPack>
+__global__ void __launch_bounds__(kCopyThreads) copy_batch_kernel(CopyBatch cb) {
+  const int64_t b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < cb.count && b >= cb.b0[i + 1]) ++i;
+  const int64_t local = b - cb.b0[i];
+  const int r = (int)(local / cb.bx[i]);
+  const int64_t row_units = cb.row_units[i];
+  const int64_t slab_rows = cb.slab_rows[i];
+  const int32_t* cu = cb.cu[i];
+  const int64_t len = (int64_t)(cu[r + 1] - cu[r]);
+  const int64_t off = cb.offsets[i] != nullptr ? (int64_t)cb.offsets[i][r] : (int64_t)cu[r];
+  const int64_t real_units = len * row_units;
+  const int64_t span_units = (!kPack && cb.zero_tail[i]) ? slab_rows * row_units : real_units;
+  const int64_t u0 = (local % cb.bx[i]) * kUnitsPerBlock;
+  if (u0 >= span_units) return;
+  const u32x4* s = kPack ? cb.src[i] + (int64_t)r * slab_rows * row_units : cb.src[i] + off * row_units;
+  u32x4* d = kPack ? cb.dst[i] + off * row_units : cb.dst[i] + (int64_t)r * slab_rows * row_units;
+  u32x4 buf[kCopyUnroll];
+#pragma unroll
+  for (int k = 0; k < kCopyUnroll; ++k) {
+    const int64_t u = u0 + k * kCopyThreads + threadIdx.x;
+    buf[k] = u < real_units ? s[u] : u32x4{};
+  }
+#pragma unroll
+  for (int k = 0; k < kCopyUnroll; ++k) {
+    const int64_t u = u0 + k * kCopyThreads + threadIdx.x;
+    if (u < span_units) __builtin_nontemporal_store(buf[k], d + u);
   }
 }
 
@@ -261,11 +310,67 @@ int copy_common(const void* src, void* dst, const int32_t* cu, const int32_t* of
   return launch_status();
 }
 
+// One launch for up to kMaxBatch copies when every one of them can move
+// 16-byte units; otherwise one launch per copy.
+template <bool kPack>
+int copy_batched(const vl_copy_desc* descs, int32_t count, hipStream_t stream) {
+  if (count < 0 || count > vl::kMaxBatch || (count > 0 && !descs)) return VL_EINVAL;
+  bool wide = true;
+  for (int32_t i = 0; i < count; ++i) {
+    const vl_copy_desc& c = descs[i];
+    if (c.num_reqs < 0 || c.num_reqs > kMaxReqs || c.row_bytes <= 0 || c.max_len < 0) return VL_EINVAL;
+    if (c.num_reqs == 0 || c.max_len == 0) continue;
+    if (!c.src || !c.dst || !c.cu_seqlens) return VL_EINVAL;
+    if (c.row_bytes % 16 != 0 || (((uintptr_t)c.src | (uintptr_t)c.dst) & 15u) != 0) wide = false;
+  }
+  if (!wide) {
+    for (int32_t i = 0; i < count; ++i) {
+      const vl_copy_desc& c = descs[i];
+      const int rc = copy_common<kPack>(c.src, c.dst, c.cu_seqlens, c.row_offsets, c.num_reqs, c.row_bytes,
+                                        c.max_len, kPack ? 0 : c.zero_fill, stream);
+      if (rc != VL_OK) return rc;
+    }
+    return VL_OK;
+  }
+  vl::CopyBatch cb{};
+  int64_t blocks = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const vl_copy_desc& c = descs[i];
+    const int n = cb.count;
+    if (c.num_reqs == 0 || c.max_len == 0) continue;
+    cb.src[n] = (const vl::u32x4*)c.src;
+    cb.dst[n] = (vl::u32x4*)c.dst;
+    cb.cu[n] = c.cu_seqlens;
+    cb.offsets[n] = c.row_offsets;
+    cb.row_units[n] = c.row_bytes / 16;
+    cb.slab_rows[n] = c.max_len;
+    cb.bx[n] = (c.max_len * cb.row_units[n] + vl::kUnitsPerBlock - 1) / vl::kUnitsPerBlock;
+    cb.zero_tail[n] = kPack ? 0 : (c.zero_fill != 0);
+    cb.b0[n] = blocks;
+    blocks += cb.bx[n] * c.num_reqs;
+    cb.count = n + 1;
+  }
+  if (cb.count == 0) return VL_OK;
+  cb.b0[cb.count] = blocks;
+  if (blocks > INT32_MAX) return VL_EUNSUPPORTED;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL((vl::copy_batch_kernel<kPack>), dim3((unsigned)blocks), dim3(vl::kCopyThreads), 0, stream, cb);
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
 
 int vl_version(void) { return 100; }
+
+int pack_by_cu_seqlens_batched(const vl_copy_desc* descs, int32_t count, vl_stream_t stream) {
+  return copy_batched<true>(descs, count, (hipStream_t)stream);
+}
+
+int unpack_by_cu_seqlens_batched(const vl_copy_desc* descs, int32_t count, vl_stream_t stream) {
+  return copy_batched<false>(descs, count, (hipStream_t)stream);
+}
 
 int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chunk_tokens,
                          int64_t max_chunks, int64_t* chunk_size, int64_t* chunk_count) {

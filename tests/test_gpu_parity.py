@@ -125,6 +125,74 @@ def test_joint_pack_with_offsets_bitexact():
     assert np.array_equal(q.cpu().view(torch.int16).numpy(), ref)
 
 
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_joint_pack_unpack_batched_bitexact(cfg):
+    """The six joint pack copies of Q, K, V (text and image pieces) in one
+    launch, and the two unpacks of the output in another, against the oracle."""
+    log(f"[pack] batched joint config {cfg}")
+    inp = wl.make_varlen_inputs(wl.CONFIGS[cfg], torch.bfloat16)
+    mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
+    hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV).reshape(-1, 2)
+    cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
+    T = inp.total_tokens
+    H, D = inp.spec.H, inp.spec.D
+    cj, ct, ci, idst = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
+    outs, items, refs = [], [], []
+    for txt, img in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img), (inp.v_text, inp.v_img)):
+        full, dst = canary_out((T, H, D), torch.bfloat16)
+        outs.append(full)
+        items += [(txt.to(DEV), cu_t, dst, cu_j[:-1]), (img.to(DEV), cu_i, dst, img_dst)]
+        ref = np.zeros((T, H, D), dtype=np.int16)
+        oracle.pack_by_cu_seqlens(txt.view(torch.int16).numpy(), ct, dst_row_offsets=cj[:-1], dst=ref)
+        oracle.pack_by_cu_seqlens(img.view(torch.int16).numpy(), ci, dst_row_offsets=idst, dst=ref)
+        refs.append(ref)
+    vl.pack_by_cu_seqlens_batched(items)
+    torch.cuda.synchronize()
+    for full, ref in zip(outs, refs):
+        assert_canary(full)
+        assert np.array_equal(full[3:3 + T].cpu().view(torch.int16).numpy(), ref)
+    flat = outs[0][3:3 + T]
+    for zero_fill in (True, False):
+        o_txt = torch.full_like(inp.q_text, 3.0, device=DEV)
+        o_img = torch.full_like(inp.q_img, 3.0, device=DEV)
+        vl.unpack_by_cu_seqlens_batched([(flat, cu_t, o_txt, cu_j[:-1]), (flat, cu_i, o_img, img_dst)],
+                                        zero_fill=zero_fill)
+        torch.cuda.synchronize()
+        three = torch.full((1,), 3.0, dtype=torch.bfloat16).view(torch.int16).numpy()[0]
+        for got, cu_ref, offs, slab in ((o_txt, ct, cj[:-1], inp.q_text), (o_img, ci, idst, inp.q_img)):
+            init = np.full(tuple(slab.shape), three, dtype=np.int16)
+            exp = oracle.unpack_by_cu_seqlens(refs[0], cu_ref, slab.shape[1], src_row_offsets=offs,
+                                              zero_fill=zero_fill, dst=init)
+            assert np.array_equal(got.cpu().view(torch.int16).numpy(), exp)
+
+
+def test_pack_batched_mixed_widths_and_empty():
+    """Copies whose rows are not whole 16-byte vectors take one launch each;
+    empty copies and requests are no-ops; the result equals single calls."""
+    log("[pack] batched mixed widths")
+    rng = np.random.default_rng(11)
+    specs = [([0, 17, 1, 300], (3,), torch.bfloat16), ([5, 0, 9], (8,), torch.bfloat16),
+             ([], (8,), torch.bfloat16), ([2, 2], (5,), torch.float32)]
+    items, singles, refs = [], [], []
+    for lengths, row, dtype in specs:
+        S = max(lengths + [1]) + 3
+        src = torch.from_numpy(rng.standard_normal((len(lengths), S) + row).astype(np.float32)).to(dtype).to(DEV)
+        cu = oracle.cu_seqlens_from_lengths(lengths)
+        cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+        T = int(cu[-1])
+        a = torch.zeros((T,) + row, dtype=dtype, device=DEV)
+        b = torch.zeros_like(a)
+        items.append((src, cu_d, a, None))
+        vl.pack_by_cu_seqlens(src, cu_d, b)
+        singles.append((a, b))
+    vl.pack_by_cu_seqlens_batched(items)
+    torch.cuda.synchronize()
+    for a, b in singles:
+        assert torch.equal(a, b)
+    with pytest.raises(vl.VarlenError):
+        vl.pack_by_cu_seqlens_batched(items * 3)
+
+
 # ------------------------------------------------------------------ tile schedule
 
 
@@ -366,12 +434,13 @@ def _pipeline(inp):
     mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
     hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV).reshape(-1, 2)
     cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
-    packed = []
+    # the launches the benchmark times: one batched pack of the six pieces
+    packed, items = [], []
     for txt, img in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img), (inp.v_text, inp.v_img)):
         dst = torch.empty((T, H, D), dtype=inp.dtype, device=DEV)
-        vl.pack_by_cu_seqlens(txt.to(DEV), cu_t, dst, dst_row_offsets=cu_j[:-1])
-        vl.pack_by_cu_seqlens(img.to(DEV), cu_i, dst, dst_row_offsets=img_dst)
+        items += [(txt.to(DEV), cu_t, dst, cu_j[:-1]), (img.to(DEV), cu_i, dst, img_dst)]
         packed.append(dst)
+    vl.pack_by_cu_seqlens_batched(items)
     q, k, v = packed
     max_len = inp.max_len
     # bf16 runs the launch the benchmark times (key split of the last round)
@@ -379,8 +448,7 @@ def _pipeline(inp):
     out, lse = fn(q, k, v, cu_j, cu_j, max_len, max_len, inp.scale, return_lse=True)
     out_txt = torch.empty_like(inp.q_text, device=DEV)
     out_img = torch.empty_like(inp.q_img, device=DEV)
-    vl.unpack_by_cu_seqlens(out, cu_t, out_txt, src_row_offsets=cu_j[:-1])
-    vl.unpack_by_cu_seqlens(out, cu_i, out_img, src_row_offsets=img_dst)
+    vl.unpack_by_cu_seqlens_batched([(out, cu_t, out_txt, cu_j[:-1]), (out, cu_i, out_img, img_dst)])
     torch.cuda.synchronize()
     return dict(cu=cu_j, q=q, k=k, v=v, out=out, lse=lse, out_txt=out_txt, out_img=out_img)
 

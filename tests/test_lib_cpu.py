@@ -73,6 +73,18 @@ def test_bad_scalars_rejected_before_launch(lib):
     assert lib.pack_by_cu_seqlens(p, 4, p, 70000, 16, p, None, None) == VL_EINVAL
     assert lib.unpack_by_cu_seqlens(p, None, p, -1, 16, p, 4, 1, None) == VL_EINVAL
     assert lib.pack_by_cu_seqlens(None, 4, None, 0, 16, None, None, None) == VL_OK
+    # batched pack / unpack: count bounds, bad descriptors, empty work
+    descs = (vl._CopyDesc * 9)()
+    assert lib.pack_by_cu_seqlens_batched(ctypes.cast(descs, ctypes.c_void_p), 9, None) == VL_EINVAL
+    assert lib.pack_by_cu_seqlens_batched(ctypes.cast(descs, ctypes.c_void_p), -1, None) == VL_EINVAL
+    assert lib.pack_by_cu_seqlens_batched(None, 2, None) == VL_EINVAL
+    assert lib.pack_by_cu_seqlens_batched(None, 0, None) == VL_OK
+    descs[0] = vl._CopyDesc(16, 16, 16, None, -4, 16, 1, 0)      # negative max_len
+    assert lib.unpack_by_cu_seqlens_batched(ctypes.cast(descs, ctypes.c_void_p), 1, None) == VL_EINVAL
+    descs[0] = vl._CopyDesc(None, 16, 16, None, 4, 16, 1, 0)     # null source with work to do
+    assert lib.pack_by_cu_seqlens_batched(ctypes.cast(descs, ctypes.c_void_p), 1, None) == VL_EINVAL
+    descs[0] = vl._CopyDesc(None, None, None, None, 4, 16, 0, 0)  # no requests: nothing to launch
+    assert lib.pack_by_cu_seqlens_batched(ctypes.cast(descs, ctypes.c_void_p), 1, None) == VL_OK
     # cu helpers
     assert lib.cu_seqlens_from_lengths(p, -1, p, None) == VL_EINVAL
     assert lib.joint_cu_seqlens(p, -1, p, 2, p, p, p, p, None) == VL_EINVAL
