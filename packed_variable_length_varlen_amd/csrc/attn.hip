@@ -26,6 +26,7 @@
 //    masks each row to [lo, hi) computed from integers (no dense mask, no
 //    device-to-host decision) and loads only the union of the rows' windows.
 #include <mutex>
+#include <type_traits>
 
 #include "vl_device.h"
 
@@ -656,6 +657,329 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   }
 }
 
+// ---------------------------------------------------------------- bf16 ping-pong kernel
+
+// Work-group barrier without a memory fence: LDS copies are waited for
+// explicitly (vmcnt) before it, and the "memory" clobber keeps the compiler
+// from moving loads or stores across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Varlen bf16 attention with 8 waves in two groups of four.  Waves w and
+// w + 4 share a SIMD, so each SIMD runs one wave of each group.  A wave
+// handles tile t in two phases: an MFMA phase (O += V(t-1)^T P(t-1)^T, then
+// S(t) = K(t) Q^T: 32 MFMAs) and a VALU phase (mask, row max, lazy rescale,
+// exp2, row sum and bf16 pack of P(t)).  Group 1 runs one phase behind group
+// 0 and every phase ends at a work-group barrier, so on each SIMD one wave
+// issues MFMAs while the other does the softmax arithmetic.
+// K and V tiles rotate through three LDS buffers each.  In phase 2j the
+// waves copy K(j+2) and V(j+1) in; those buffers last held K(j-1) and
+// V(j-2), which both groups finished in phases 2j-2 and 2j-1.  At the end of
+// phase 2j each wave waits for its copies of phase 2j-2, so K(j+1) and V(j)
+// are complete for phase 2j+2, where group 0 first reads them.  The phase
+// loop is unrolled six times so every LDS access names one __shared__ array
+// and the compiler's LDS-copy waits stay precise.
+template <int D, int BN>
+__global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
+  using G = Bf16Geo<D, 8, BN>;
+  constexpr int BM = 256;
+  constexpr int L = G::kLoadsPerWave;
+  __shared__ __attribute__((aligned(16))) char k0[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char k1[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char k2[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v0[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char v2[G::kTileBytes];
+
+  const TileRange tr = tile_range<BM, BN, false>(a);
+  if (!tr.valid) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int ql = lane & 31;
+  const int g = lane >> 5;
+  const int H = a.H;
+  const int h = tr.h;
+  const int64_t row_stride = (int64_t)H * D;
+  const int my_row = tr.q0 + wave * 32 + ql;
+  const bool wave_active = tr.q0 + wave * 32 < tr.q1;
+
+  // Q operand of S^T = K Q^T: lane (ql, g) holds features ds*16 + 8g .. +7.
+  bf16x8 qf[G::NDS];
+  {
+    const int qrow = min(my_row, tr.q1 - 1);
+    const bf16x8* qp = (const bf16x8*)((const __bf16*)a.q + (int64_t)qrow * row_stride + (int64_t)h * D + g * 8);
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds) qf[ds] = qp[2 * ds];
+  }
+
+  // Copy offsets (see the 4-wave kernel): wave w's load i fills LDS bytes
+  // [(L*w + i) KB, +1 KB) of a tile buffer.
+  const int ld_row_in_blk = lane / G::CPR;
+  const int ld_pchunk = lane % G::CPR;
+  const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
+  // Prologue copies: all 8 waves, L loads each per tile.
+  uint32_t ld_koff[L], ld_voff[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int row = (L * wave + i) * G::RPI + ld_row_in_blk;
+    ld_koff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ k_swz<G::CPR>(row)) * 16;
+    ld_voff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(row)) * 16;
+  }
+  // Loop copies: the four waves of one group move a whole tile, 2L loads each;
+  // group 1 copies K (rows by K swizzle), group 0 copies V.
+  constexpr int L2 = 2 * L;
+  const int gw = wave & 3;
+  uint32_t ld_goff[L2];
+#pragma unroll
+  for (int i = 0; i < L2; ++i) {
+    const int row = (L2 * gw + i) * G::RPI + ld_row_in_blk;
+    const int swz = grp == 1 ? k_swz<G::CPR>(row) : v_swz<G::CPR>(row);
+    ld_goff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ swz) * 16;
+  }
+  const char* kbase = (const char*)a.k + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
+  const char* vbase = (const char*)a.v + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
+  const int nkeys = tr.k_hi - tr.k_lo;
+  const int ntiles = (nkeys + BN - 1) / BN;
+  const bool ragged = (nkeys % BN) != 0;
+  // Source and byte count of tile `tile`; past the last tile a zero-byte
+  // descriptor reads nothing (the copy still issues, keeping wait counts uniform).
+  auto tile_src = [&](const char* base, int tile, const char*& src, int& nb) {
+    const bool ok = tile < ntiles;
+    src = ok ? base + (int64_t)(tr.k_lo + tile * BN) * rs_bytes : base;
+    nb = ok ? (min(BN, nkeys - tile * BN) - 1) * (int)rs_bytes + G::ROW : 0;
+  };
+  // Tile `tile` of K or V into dst, this wave's share of an all-wave copy.
+  auto copy_tile = [&](const char* base, int tile, char* dst, const uint32_t(&off)[L]) {
+    const bool ok = tile < ntiles;
+    const char* src = ok ? base + (int64_t)(tr.k_lo + tile * BN) * rs_bytes : base;
+    const int nb = ok ? (min(BN, nkeys - tile * BN) - 1) * (int)rs_bytes + G::ROW : 0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) lds_dma_one(src, nb, dst + (L * wave + i) * 1024, off[i]);
+  };
+
+  // LDS read offsets of the MFMA operands (see the 4-wave kernel).
+  int k_rd[G::NDS];
+#pragma unroll
+  for (int ds = 0; ds < G::NDS; ++ds) k_rd[ds] = ql * G::ROW + (((2 * ds + g) ^ k_swz<G::CPR>(ql)) * 16);
+  const int vgrp = lane >> 4;
+  const int gi = lane & 15;
+  const int v_row = 4 * (vgrp >> 1) + (gi >> 2);
+  int v_rd[G::NDB];
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) {
+    const int byte_in_row = db * 64 + 32 * (vgrp & 1) + 8 * (gi & 3);
+    const int chunk = (byte_in_row >> 4) ^ v_swz<G::CPR>(v_row);
+    v_rd[db] = v_row * G::ROW + chunk * 16 + (byte_in_row & 15);
+  }
+
+  RowState<G::NKB, G::NDB> st;
+  st.init();
+  f32x16 s[G::NKB];
+  bf16x8 pf[G::NKC];
+
+  // ---- MFMA phase of tile k: PV of tile k-1 (V in vl), then S of tile k (K in kl).
+  auto m_phase = [&](int k, const char* kl, const char* vl) {
+    if (k >= 1 && k <= ntiles) {
+      constexpr int VPF = 6;
+      constexpr int NSTEP = G::NKC * G::NDB;
+      auto read_v = [&](int step) {
+        const char* p = vl + (step / G::NDB) * 16 * G::ROW + v_rd[step % G::NDB];
+        const i16x4 lo4 = lds_read_tr(p);
+        const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 va[VPF + 1];
+#pragma unroll
+      for (int step = 0; step < VPF; ++step) va[step] = read_v(step);
+#pragma unroll
+      for (int step = 0; step < NSTEP; ++step) {
+        if (step + VPF < NSTEP) va[(step + VPF) % (VPF + 1)] = read_v(step + VPF);
+        VL_SCHED_BARRIER(0);
+        st.o[step % G::NDB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[step / G::NDB], st.o[step % G::NDB], 0, 0, 0);
+        VL_SCHED_BARRIER(0);
+      }
+    }
+    if (k < ntiles) {
+      constexpr int KPF = 3;
+      constexpr int NSTEP = G::NKB * G::NDS;
+      auto read_k = [&](int step) {
+        return *(const bf16x8*)(kl + (step % G::NKB) * 32 * G::ROW + k_rd[step / G::NKB]);
+      };
+#pragma unroll
+      for (int kb = 0; kb < G::NKB; ++kb) s[kb] = f32x16{};
+      bf16x8 ka[KPF + 1];
+#pragma unroll
+      for (int step = 0; step < KPF; ++step) ka[step] = read_k(step);
+#pragma unroll
+      for (int step = 0; step < NSTEP; ++step) {
+        if (step + KPF < NSTEP) ka[(step + KPF) % (KPF + 1)] = read_k(step + KPF);
+        VL_SCHED_BARRIER(0);
+        s[step % G::NKB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[step / G::NKB], s[step % G::NKB], 0, 0, 0);
+        VL_SCHED_BARRIER(0);
+      }
+    }
+  };
+
+  // ---- VALU phase of tile k: scores -> probabilities P(k) in bf16.  The
+  // group's tile copy (copy(i), i < 2L) is issued spread over the exp loop.
+  auto v_phase = [&](int k, auto&& copy) {
+    if (!wave_active || k < 0 || k >= ntiles) {
+#pragma unroll
+      for (int i = 0; i < L2; ++i) copy(i);
+      return;
+    }
+    // The empty asm statements keep the two rare paths (the sequence's last,
+    // partial tile; a rescale) real branches: if-converted, their compares,
+    // selects and 64 multiplies would run on every tile.
+    if (ragged && k == ntiles - 1) {
+      asm volatile("");
+      mask_scores<G::NKB>(s, tr.k_lo + k * BN, g, tr.k_lo, tr.k_hi);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+    mx = pair_max(mx);
+    const float mx_c = mx * a.c;
+    const bool need = mx_c > st.m_c + 8.0f;
+    if (__ballot(need)) {
+      asm volatile("");
+      const float m_new = need ? mx_c : st.m_c;
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_c - m_new) : 1.0f;
+      st.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < G::NDB; ++d) st.o[d] *= alpha;
+      st.m_c = m_new;
+    }
+    const float neg_m = (st.m_c == -INFINITY) ? 0.f : -st.m_c;
+    float ls0 = 0.f, ls1 = 0.f;
+    constexpr int kCopyEvery = G::NKB * 16 / L2;
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if ((kb * 16 + j) % kCopyEvery == 0) copy((kb * 16 + j) / kCopyEvery);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][j], a.c, neg_m));
+        s[kb][j] = p;
+        if (j & 1)
+          ls1 += p;
+        else
+          ls0 += p;
+      }
+#pragma unroll
+    for (int kc = 0; kc < G::NKC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][8 * (kc & 1) + e];
+    st.l += ls0 + ls1;
+  };
+
+  // ---- phase p0 + I of group GR (I, GR compile-time).  The MFMA phase of
+  // phase p works on tile p/2: K buffer (p/2) % 3, V buffer (p/2 - 1) % 3.
+  // The group in its VALU phase copies: in even phase p (group 1) K(p/2 + 2),
+  // in odd phase p (group 0) V(p/2 + 1); it then waits for the copies it
+  // issued two phases before, which the MFMA phase of phase p + 1 or later
+  // reads first.  Then the barrier.
+  auto phase = [&](int p0, auto I_, auto GR_) {
+    constexpr int I = decltype(I_)::value;
+    constexpr int GR = decltype(GR_)::value;
+    char* const kbuf[3] = {k0, k1, k2};
+    char* const vbuf[3] = {v0, v1, v2};
+    const int p = p0 + I;
+    if constexpr (((I - GR) & 1) == 0) {
+      if (wave_active) m_phase((p - GR) / 2, kbuf[(I / 2) % 3], vbuf[(I / 2 + 2) % 3]);
+    } else {
+      const char* src;
+      int nb;
+      char* dst;
+      if constexpr ((I & 1) == 0) {
+        tile_src(kbase, p / 2 + 2, src, nb);
+        dst = kbuf[(I / 2 + 2) % 3];
+      } else {
+        tile_src(vbase, p / 2 + 1, src, nb);
+        dst = vbuf[(I / 2 + 1) % 3];
+      }
+      v_phase((p - GR - 1) / 2, [&](int i) { lds_dma_one(src, nb, dst + (L2 * gw + i) * 1024, ld_goff[i]); });
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | L2);
+    }
+    wg_barrier();
+  };
+  const int nphase = 2 * ntiles + 2;
+  auto run = [&](auto GR) {
+    using IC0 = std::integral_constant<int, 0>;
+    using IC1 = std::integral_constant<int, 1>;
+    using IC2 = std::integral_constant<int, 2>;
+    using IC3 = std::integral_constant<int, 3>;
+    using IC4 = std::integral_constant<int, 4>;
+    using IC5 = std::integral_constant<int, 5>;
+    for (int p0 = 0; p0 < nphase; p0 += 6) {
+      phase(p0, IC0{}, GR);
+      if (p0 + 1 >= nphase) break;
+      phase(p0, IC1{}, GR);
+      if (p0 + 2 >= nphase) break;
+      phase(p0, IC2{}, GR);
+      if (p0 + 3 >= nphase) break;
+      phase(p0, IC3{}, GR);
+      if (p0 + 4 >= nphase) break;
+      phase(p0, IC4{}, GR);
+      if (p0 + 5 >= nphase) break;
+      phase(p0, IC5{}, GR);
+    }
+  };
+
+  copy_tile(kbase, 0, k0, ld_koff);
+  copy_tile(kbase, 1, k1, ld_koff);
+  copy_tile(vbase, 0, v0, ld_voff);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  wg_barrier();
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  if (!wave_active) return;
+  const float l_tot = pair_sum(st.l);
+  if (tr.unit >= 0) {
+    float* wo = a.ws + (int64_t)tr.unit * BM * D;
+    float2* wml = (float2*)(a.ws + (int64_t)a.slots * BM * D) + (int64_t)tr.unit * BM;
+    if (my_row < tr.q1) {
+      const int r = my_row - tr.q0;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = db * 32 + 8 * i + 4 * g;
+          *(f32x4*)(wo + (int64_t)r * D + d) =
+              f32x4{st.o[db][4 * i], st.o[db][4 * i + 1], st.o[db][4 * i + 2], st.o[db][4 * i + 3]};
+        }
+      if (g == 0) wml[r] = make_float2(st.m_c, l_tot);
+    }
+    return;
+  }
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (my_row < tr.q1) {
+    __bf16* op = (__bf16*)a.out + (int64_t)my_row * row_stride + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + 8 * i + 4 * g;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[db][4 * i + e] * inv);
+        *(bf16x4*)(op + d) = w;
+      }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(int64_t)my_row * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 kernel
 
 template <int D>
@@ -889,10 +1213,11 @@ __global__ void __launch_bounds__(64) tile_map_kernel(const int32_t* q_cu, const
 namespace {
 
 constexpr int kChunk = 16;  // logical tiles kept together on one chiplet
-constexpr int kBf16VarlenWaves = 4;  // waves per work-group of the bf16 varlen kernel
-constexpr int kBf16VarlenQB = 1;     // 32-row query blocks per wave: 128 rows per work-group
-constexpr int kBf16VarlenBN = 64;    // keys per tile of the bf16 varlen kernel
-constexpr int kBf16VarlenBM = 32 * kBf16VarlenWaves * kBf16VarlenQB;
+// bf16 varlen: the ping-pong kernel, 8 waves, 256 query rows per work-group,
+// 64-key tiles
+constexpr int kBf16VarlenThreads = 512;
+constexpr int kBf16VarlenBN = 64;
+constexpr int kBf16VarlenBM = 256;
 constexpr int kF32Waves = 4;
 constexpr int kMaxDevices = 64;
 
@@ -900,7 +1225,7 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 template <int D>
 constexpr auto bf16_varlen_kernel() {
-  return &vl::attn_bf16_kernel<D, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>;
+  return &vl::attn_bf16_pp_kernel<D, kBf16VarlenBN>;
 }
 
 // Work-groups of the bf16 varlen kernel resident at once on the current
@@ -920,8 +1245,8 @@ int bf16_varlen_slots(int D) {
   int cus = 0, per_cu = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bf16_varlen_kernel<128>(), kBf16VarlenWaves * 64, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bf16_varlen_kernel<64>(), kBf16VarlenWaves * 64, 0);
+    e = D == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bf16_varlen_kernel<128>(), kBf16VarlenThreads, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bf16_varlen_kernel<64>(), kBf16VarlenThreads, 0);
   if (e != hipSuccess || cus <= 0 || per_cu <= 0) {
     (void)hipGetLastError();
     return 0;
@@ -942,9 +1267,8 @@ struct VarlenPlan {
 inline VarlenPlan varlen_plan(bool f32, bool split, int64_t num_reqs, int64_t max_q, int64_t max_kv, int64_t H,
                               int D) {
   VarlenPlan p;
-  const int waves = f32 ? kF32Waves : kBf16VarlenWaves;
-  p.block_m = f32 ? 32 * waves : kBf16VarlenBM;
-  p.threads = 64 * waves;
+  p.block_m = f32 ? 32 * kF32Waves : kBf16VarlenBM;
+  p.threads = f32 ? 64 * kF32Waves : kBf16VarlenThreads;
   // a split needs at least two key ranges of kMinSplitKeys keys
   p.slots = (split && !f32 && max_kv / vl::kMinSplitKeys >= 2) ? bf16_varlen_slots(D) : 0;
   p.blocks = (num_reqs == 0 || max_q == 0) ? 0 : vl::grid_blocks(num_reqs, max_q, H, p.block_m, kChunk, p.slots);
@@ -1002,11 +1326,11 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
     return launch_status();
   }
   if (D == 128)
-    hipLaunchKernelGGL((vl::attn_bf16_kernel<128, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>),
-                       dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
+    hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<128, kBf16VarlenBN>), dim3((unsigned)G), dim3(plan.threads), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((vl::attn_bf16_kernel<64, kBf16VarlenWaves, kBf16VarlenQB, kBf16VarlenBN, false>),
-                       dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
+    hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<64, kBf16VarlenBN>), dim3((unsigned)G), dim3(plan.threads), 0,
+                       stream, a);
   if (plan.slots > 0) {
     // one block per possible tail tile; blocks past the tail return at once
     if (D == 128)
