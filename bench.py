@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4])
+    ap.add_argument("--workload", default="joint-16k", choices=["joint-16k", "mixres-4req", "edit-cfg-4seq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
@@ -151,8 +151,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    spec = wl.CONFIGS[args.config]
-    err(f"[bench] generating config {args.config} ({spec.name})")
+    spec = wl.WORKLOADS[args.workload]
+    err(f"[bench] generating {args.workload} ({spec.name})")
     inp = wl.make_varlen_inputs(spec, torch.bfloat16)
     H, D = spec.H, spec.D
     R = inp.R
@@ -176,7 +176,7 @@ def main():
     # partial results of the key split of the last round (allocated once)
     workspace = torch.empty(max(vl.varlen_split_workspace_bytes(D), 1), dtype=torch.uint8, device=dev)
 
-    bl_spec = wl.BLOCK_LOCAL_CONFIGS[5]
+    bl_spec = wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"]
     bl = wl.make_block_local_inputs(bl_spec, torch.bfloat16)
     bq, bk, bv = bl.q.to(dev), bl.k.to(dev), bl.v.to(dev)
     bouts = [torch.empty_like(bq) for _ in bl_spec.windows]
@@ -249,8 +249,8 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
     value = step_flop / (dt / args.steps) / 1e12
     achieved = flop_varlen / (attn_ms * 1e-3) / 1e12
-    workload = f"config{args.config}:{spec.name}+blocklocal-n2003-b24-h16-d64-4windows"
-    traffic = load_traffic(f"config{args.config}")
+    workload = f"{spec.name}+{bl_spec.name}-4windows"
+    traffic = load_traffic(args.workload)
 
     err(f"[bench] step {ms_per_step:.3f} ms, attention {attn_ms:.3f} ms = {achieved:.1f} TFLOP/s "
         f"({100 * achieved / BF16_PEAK_TFLOPS:.1f}% of bf16 peak); pairs {pairs}")
@@ -291,7 +291,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_bf16_kernel<128, 4, 1, 64, false> + split_merge_kernel (varlen_attn_fwd_split)",
+            "kernel": "attn_bf16_pp_kernel<128, 64> + split_merge_kernel<128, 256> (varlen_attn_fwd_split)",
             "kernel_ms": round(attn_ms, 4),
         },
         "cpu_baseline": cpu,

@@ -1144,49 +1144,54 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- split merge
 
-// Merges the partial results of the split work items: block b < tail takes
-// tile full + b, whose key ranges ran as units b*parts .. b*parts+parts-1.
-// Per row, with exponent offsets m_p (log2 units) and row sums l_p of the
-// parts: m = max m_p, w_p = 2^(m_p - m), out = sum_p w_p O_p / sum_p w_p l_p,
-// lse = (m + log2 sum_p w_p l_p) ln 2.  Empty parts carry m_p = -inf, l_p = 0.
+// Merges the partial results of the split work items.  Tail tile t's key
+// ranges ran as units t*parts .. t*parts + parts - 1; a block handles RPB rows
+// of one tail tile, a thread one 4-float group of a row.  Per row, with
+// exponent offsets m_p (log2 units) and row sums l_p of the parts:
+// m = max m_p, w_p = 2^(m_p - m), out = sum_p w_p O_p / sum_p w_p l_p,
+// lse = (m + log2 sum_p w_p l_p) ln 2 -- taken in one pass over the parts with
+// a running maximum.  Empty parts carry m_p = -inf, l_p = 0 and are skipped.
 template <int D, int BM>
 __global__ void __launch_bounds__(256) split_merge_kernel(AttnArgs a) {
+  constexpr int C4 = D / 4;         // 4-float groups per row
+  constexpr int RPB = 256 / C4;     // rows per block
+  constexpr int BPT = BM / RPB;     // blocks per tail tile
   const SplitPlan sp = split_plan(total_tiles(a.q_cu, a.R, a.H, BM), a.slots, a.max_kv);
-  if (sp.parts < 2 || (int)blockIdx.x >= sp.tail) return;
+  const int t = (int)blockIdx.x / BPT;
+  if (sp.parts < 2 || t >= sp.tail) return;
   int req, head, qt;
-  find_tile(a.q_cu, a.kv_cu, a.R, a.H, BM, sp.full + (int)blockIdx.x, req, head, qt);
+  find_tile(a.q_cu, a.kv_cu, a.R, a.H, BM, sp.full + t, req, head, qt);
   if (req < 0) return;
   const int q0 = a.q_cu[req] + qt * BM;
   const int rows = min(a.q_cu[req + 1], q0 + BM) - q0;
-  const int64_t u0 = (int64_t)blockIdx.x * sp.parts;
+  const int r = ((int)blockIdx.x % BPT) * RPB + (int)threadIdx.x / C4;
+  const int c = (int)threadIdx.x % C4;
+  if (r >= rows) return;
+  const int64_t u0 = (int64_t)t * sp.parts;
   const float2* wml = (const float2*)(a.ws + (int64_t)a.slots * BM * D);
-  const int64_t row_stride = (int64_t)a.H * D;
-  constexpr int C4 = D / 4;  // 4-float groups per row
-  for (int f = threadIdx.x; f < rows * C4; f += 256) {
-    const int r = f / C4;
-    const int c = f % C4;
-    float m = -INFINITY;
-    for (int p = 0; p < sp.parts; ++p) m = fmaxf(m, wml[(u0 + p) * BM + r].x);
-    f32x4 acc = f32x4{};
-    float l = 0.f;
-    if (m != -INFINITY) {
-      for (int p = 0; p < sp.parts; ++p) {
-        const float2 ml = wml[(u0 + p) * BM + r];
-        const float w = __builtin_amdgcn_exp2f(ml.x - m);
-        l = fmaf(w, ml.y, l);
-        const f32x4 o = *(const f32x4*)(a.ws + ((u0 + p) * BM + r) * D + 4 * c);
-        acc += w * o;
-      }
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc = f32x4{};
+  for (int p = 0; p < sp.parts; ++p) {
+    const float2 ml = wml[(u0 + p) * BM + r];
+    if (ml.x == -INFINITY) continue;
+    if (ml.x > m) {
+      const float sc = __builtin_amdgcn_exp2f(m - ml.x);  // 0 while m = -inf
+      acc *= sc;
+      l *= sc;
+      m = ml.x;
     }
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = (__bf16)(acc[e] * inv);
-    *(bf16x4*)((__bf16*)a.out + (int64_t)(q0 + r) * row_stride + (int64_t)head * D + 4 * c) = y;
-    if (c == 0 && a.lse != nullptr)
-      a.lse[(int64_t)(q0 + r) * a.H + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    const float w = __builtin_amdgcn_exp2f(ml.x - m);
+    l = fmaf(w, ml.y, l);
+    acc += w * *(const f32x4*)(a.ws + ((u0 + p) * BM + r) * D + 4 * c);
   }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = (__bf16)(acc[e] * inv);
+  *(bf16x4*)((__bf16*)a.out + (int64_t)(q0 + r) * a.H * D + (int64_t)head * D + 4 * c) = y;
+  if (c == 0 && a.lse != nullptr)
+    a.lse[(int64_t)(q0 + r) * a.H + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- tile-map export
@@ -1332,13 +1337,13 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
     hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<64, kBf16VarlenBN>), dim3((unsigned)G), dim3(plan.threads), 0,
                        stream, a);
   if (plan.slots > 0) {
-    // one block per possible tail tile; blocks past the tail return at once
+    // BM / (256 / (D/4)) blocks per possible tail tile (there are fewer than
+    // slots of them); blocks past the tail return at once
+    const unsigned mb = (unsigned)plan.slots * (unsigned)(kBf16VarlenBM * D / 4 / 256);
     if (D == 128)
-      hipLaunchKernelGGL((vl::split_merge_kernel<128, kBf16VarlenBM>), dim3((unsigned)plan.slots), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((vl::split_merge_kernel<128, kBf16VarlenBM>), dim3(mb), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((vl::split_merge_kernel<64, kBf16VarlenBM>), dim3((unsigned)plan.slots), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((vl::split_merge_kernel<64, kBf16VarlenBM>), dim3(mb), dim3(256), 0, stream, a);
   }
   return launch_status();
 }

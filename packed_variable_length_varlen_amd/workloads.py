@@ -4,8 +4,8 @@ This module only draws random numbers and lays them out; it holds none of the
 attention, packing or boundary arithmetic.  Both the GPU path and the CPU
 oracle are fed from what it returns.
 
-Recipe (all configurations):
-  * rng = numpy.random.default_rng(seed), seed = configuration number;
+Recipe (all workloads):
+  * rng = numpy.random.default_rng(seed), seed = the spec's seed field;
   * per-request text lengths are drawn first, in request order, with
     rng.integers(lo, hi + 1);
   * then Q, K and V are drawn in that order, each as float32 standard normals,
@@ -55,25 +55,25 @@ class BlockLocalSpec:
     seed: int
 
 
-CONFIGS = {
+WORKLOADS = {
     # 3 packed requests of 17, 64 and 129 tokens (text-only pieces), H=2, D=64.
-    1: VarlenSpec("tiny-3req-17-64-129-h2-d64", 2, 64,
+    "tiny-3req": VarlenSpec("tiny-3req-17-64-129-h2-d64", 2, 64,
                   [(17, 17), (64, 64), (129, 129)], [(0, 0), (0, 0), (0, 0)], 1),
     # One joint request: 2048x2048 image -> 128x128 grid, text 8..256.
-    2: VarlenSpec("joint-1req-2048sq-16384img-text8-256-h24-d128", 24, 128,
+    "joint-16k": VarlenSpec("joint-1req-2048sq-16384img-text8-256-h24-d128", 24, 128,
                   [(8, 256)], [(128, 128)], 2),
     # Mixed resolutions: 64x64, 83x83, 128x128, 48x84 grids, each after text 8..256.
-    3: VarlenSpec("mixres-4req-4096-6889-16384-4032img-h24-d128", 24, 128,
+    "mixres-4req": VarlenSpec("mixres-4req-4096-6889-16384-4032img-h24-d128", 24, 128,
                   [(8, 256)] * 4, [(64, 64), (83, 83), (128, 128), (48, 84)], 3),
     # Edit-style CFG halves [r1+, r1-, r2+, r2-]: 2x16,384 image tokens each
     # (noise + source latents, a 256x128 grid), positive text 8..256,
     # negative text 1..8.
-    4: VarlenSpec("edit-cfg-4seq-32768img-h24-d128", 24, 128,
+    "edit-cfg-4seq": VarlenSpec("edit-cfg-4seq-32768img-h24-d128", 24, 128,
                   [(8, 256), (1, 8), (8, 256), (1, 8)], [(256, 128)] * 4, 4),
 }
 
-BLOCK_LOCAL_CONFIGS = {
-    5: BlockLocalSpec("dit-blocklocal-n2003-b24-h16-d64", 1, 2003, 16, 64, 24,
+BLOCK_LOCAL_WORKLOADS = {
+    "vocoder-dit": BlockLocalSpec("dit-blocklocal-n2003-b24-h16-d64", 1, 2003, 16, 64, 24,
                       [(0, 0), (1, 0), (0, 1), (1, 1)], 5),
 }
 

@@ -41,11 +41,11 @@ def assert_canary(full, pad=3):
 # ------------------------------------------------------------------ boundaries
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", ["tiny-3req", "joint-16k", "mixres-4req", "edit-cfg-4seq"])
 def test_joint_cu_seqlens_bitexact(cfg):
-    log(f"[joint_cu] config {cfg}")
-    spec = wl.CONFIGS[cfg]
-    rng = np.random.default_rng(cfg)
+    log(f"[joint_cu] {cfg}")
+    spec = wl.WORKLOADS[cfg]
+    rng = np.random.default_rng(spec.seed)
     R = len(spec.img_grids)
     mask = np.zeros((R, wl.TEXT_CAP), dtype=bool)
     for r, (lo, hi) in enumerate(spec.text_ranges):
@@ -108,7 +108,7 @@ def test_pack_unpack_bitexact_vector_widths(row_shape, dtype):
 
 def test_joint_pack_with_offsets_bitexact():
     log("[pack] joint text+image with offsets")
-    inp = wl.make_varlen_inputs(wl.CONFIGS[3], torch.bfloat16)
+    inp = wl.make_varlen_inputs(wl.WORKLOADS["mixres-4req"], torch.bfloat16)
     mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
     hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV)
     cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
@@ -125,12 +125,12 @@ def test_joint_pack_with_offsets_bitexact():
     assert np.array_equal(q.cpu().view(torch.int16).numpy(), ref)
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", ["joint-16k", "mixres-4req"])
 def test_joint_pack_unpack_batched_bitexact(cfg):
     """The six joint pack copies of Q, K, V (text and image pieces) in one
     launch, and the two unpacks of the output in another, against the oracle."""
-    log(f"[pack] batched joint config {cfg}")
-    inp = wl.make_varlen_inputs(wl.CONFIGS[cfg], torch.bfloat16)
+    log(f"[pack] batched joint {cfg}")
+    inp = wl.make_varlen_inputs(wl.WORKLOADS[cfg], torch.bfloat16)
     mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
     hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV).reshape(-1, 2)
     cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
@@ -258,18 +258,18 @@ def _run_varlen(q, k, v, q_cu, kv_cu, scale, f32, max_q=None, max_kv=None, split
 
 
 @pytest.mark.parametrize("f32", [False, True])
-def test_varlen_tiny_config_full(f32):
+def test_varlen_tiny_workload_full(f32):
     dtype = torch.float32 if f32 else torch.bfloat16
-    log(f"[varlen] config 1 {dtype}")
-    inp = wl.make_varlen_inputs(wl.CONFIGS[1], dtype)
+    log(f"[varlen] tiny-3req {dtype}")
+    inp = wl.make_varlen_inputs(wl.WORKLOADS["tiny-3req"], dtype)
     cu, cu_t, _, _ = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
     q = torch.from_numpy(oracle.pack_by_cu_seqlens(inp.q_text.float().numpy(), cu_t)).to(dtype)
     k = torch.from_numpy(oracle.pack_by_cu_seqlens(inp.k_text.float().numpy(), cu_t)).to(dtype)
     v = torch.from_numpy(oracle.pack_by_cu_seqlens(inp.v_text.float().numpy(), cu_t)).to(dtype)
     out, lse = _run_varlen(q, k, v, cu, cu, inp.scale, f32)
     ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), cu, cu, inp.scale)
-    mx, mean = check_close(to64(out), ro, f32, "config 1")
-    check_lse(to64(lse), rl, f32, "config 1")
+    mx, mean = check_close(to64(out), ro, f32, "tiny-3req")
+    check_lse(to64(lse), rl, f32, "tiny-3req")
     log(f"   max-abs {mx:.3g} mean-abs {mean:.3g}")
 
 
@@ -453,11 +453,11 @@ def _pipeline(inp):
     return dict(cu=cu_j, q=q, k=k, v=v, out=out, lse=lse, out_txt=out_txt, out_img=out_img)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_configs_sampled(cfg):
-    log(f"[pipeline] config {cfg}: generating inputs")
-    inp = wl.make_varlen_inputs(wl.CONFIGS[cfg], torch.bfloat16)
-    log(f"[pipeline] config {cfg}: T={inp.total_tokens} running GPU path")
+@pytest.mark.parametrize("cfg", ["joint-16k", "mixres-4req", "edit-cfg-4seq"])
+def test_full_size_workloads_sampled(cfg):
+    log(f"[pipeline] {cfg}: generating inputs")
+    inp = wl.make_varlen_inputs(wl.WORKLOADS[cfg], torch.bfloat16)
+    log(f"[pipeline] {cfg}: T={inp.total_tokens} running GPU path")
     res = _pipeline(inp)
     cj, ct, ci, idst = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
     assert np.array_equal(res["cu"].cpu().numpy(), cj.astype(np.int32))
@@ -473,11 +473,11 @@ def test_full_size_configs_sampled(cfg):
     assert np.array_equal(res["k"].float().cpu().numpy(), kn)
     assert np.array_equal(res["v"].float().cpu().numpy(), vn)
     rows = sample_rows(cj)
-    log(f"[pipeline] config {cfg}: oracle on {rows.size} sampled rows")
+    log(f"[pipeline] {cfg}: oracle on {rows.size} sampled rows")
     ro, rl = oracle.varlen_attention(qn, kn, vn, cj, cj, inp.scale, rows=rows)
     out = res["out"].float().cpu().numpy()[rows].astype(np.float64)
-    mx, mean = check_close(out, ro, False, f"config {cfg}")
-    check_lse(res["lse"].cpu().numpy()[rows].astype(np.float64), rl, False, f"config {cfg}")
+    mx, mean = check_close(out, ro, False, f"{cfg}")
+    check_lse(res["lse"].cpu().numpy()[rows].astype(np.float64), rl, False, f"{cfg}")
     log(f"   max-abs {mx:.3g} mean-abs {mean:.3g}")
     # unpack is the exact inverse on the real rows and zero on the padding
     out_full = res["out"].cpu()
@@ -499,7 +499,7 @@ def test_block_local_vs_oracle(n, win, f32):
     dtype = torch.float32 if f32 else torch.bfloat16
     lb, la = win
     log(f"[block_local] n={n} win={win} {dtype}")
-    spec = wl.BLOCK_LOCAL_CONFIGS[5]
+    spec = wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"]
     inp = wl.make_block_local_inputs(spec, dtype, n=n, seed=1000 + n)
     full, out = canary_out(tuple(inp.q.shape), dtype, pad=1)
     fn = vl.block_local_attn_fwd_f32 if f32 else vl.block_local_attn_fwd
@@ -652,7 +652,7 @@ def test_block_local_production_shape(f32):
     (167 blocks of 24, last block 16 frames), own-block and one-neighbour layers."""
     dtype = torch.float32 if f32 else torch.bfloat16
     log(f"[block_local] production shape {dtype}")
-    spec = wl.BLOCK_LOCAL_CONFIGS[5]
+    spec = wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"]
     inp = wl.make_block_local_inputs(spec, dtype, n=4000, B=2, seed=4000)
     for lb, la in [(0, 0), (1, 0), (0, 1)]:
         out = vl.block_local_attn_fwd_f32(inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV), 24, lb, la, inp.scale) if f32 \

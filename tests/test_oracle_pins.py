@@ -231,8 +231,8 @@ def _brute_varlen(q, k, v, q_cu, kv_cu, scale):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_varlen_matches_block_diagonal_brute_force_on_tiny_config(dtype):
-    inp = wl.make_varlen_inputs(wl.CONFIGS[1], dtype)
+def test_varlen_matches_block_diagonal_brute_force_on_tiny_workload(dtype):
+    inp = wl.make_varlen_inputs(wl.WORKLOADS["tiny-3req"], dtype)
     mask = inp.text_mask
     cu, cu_text, _, _ = oracle.joint_cu_seqlens(mask, inp.img_hw)
     q = oracle.pack_by_cu_seqlens(_np(inp.q_text), cu_text)
@@ -399,11 +399,11 @@ def test_block_local_key_ranges_by_enumeration():
             assert allowed == list(range(lo, hi))
 
 
-def test_block_local_config5_sampled_rows_against_mask():
-    inp = wl.make_block_local_inputs(wl.BLOCK_LOCAL_CONFIGS[5], torch.bfloat16)
+def test_block_local_vocoder_sampled_rows_against_mask():
+    inp = wl.make_block_local_inputs(wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"], torch.bfloat16)
     q, k, v = (_np(t)[0].astype(np.float64) for t in (inp.q, inp.k, inp.v))
     n = q.shape[0]
-    for lb, la in wl.BLOCK_LOCAL_CONFIGS[5].windows:
+    for lb, la in wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"].windows:
         o, _ = oracle.block_local_attention(_np(inp.q), _np(inp.k), _np(inp.v), 24, lb, la, inp.scale)
         for i in (0, 23, 24, 1000, 1991, 1992, 2002):
             keys = [j for j in range(n) if -lb <= j // 24 - i // 24 <= la]
