@@ -422,6 +422,8 @@ def test_cfg_combine_endpoints_and_linearity():
     assert np.array_equal(oracle.cfg_combine(p, n, 0.0), n)
     np.testing.assert_allclose(oracle.cfg_combine(p, n, 1.0), p, atol=1e-15)
     np.testing.assert_allclose(oracle.cfg_combine(p, n, 4.0) - oracle.cfg_combine(p, n, 3.0), p - n, atol=1e-14)
+    # by hand, with scale 2.5: 1 + 2.5*(2 - 1) = 3.5 and 3 + 2.5*(-1 - 3) = -7
+    assert np.array_equal(oracle.cfg_combine(np.array([2.0, -1.0]), np.array([1.0, 3.0]), 2.5), [3.5, -7.0])
 
 
 # ---------------------------------------------------------------- planted mistakes
