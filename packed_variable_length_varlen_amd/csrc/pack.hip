@@ -12,7 +12,7 @@
 namespace vl {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;  // 16-byte loads in flight per thread (4 streams HBM best; 8 is slower)
+constexpr int kCopyUnroll = 2;  // 16-byte loads in flight per thread: 2 beats 4 and 8 on large copies
 constexpr int kUnitsPerBlock = kCopyThreads * kCopyUnroll;
 
 // Request r = blockIdx.y copies units [0, len_r*row_units) of its slab in

@@ -193,6 +193,36 @@ def test_pack_batched_mixed_widths_and_empty():
         vl.pack_by_cu_seqlens_batched(items * 3)
 
 
+def test_batched_copies_many_pairs():
+    """More (copy, request) pairs than the compact path takes (3 x 1000
+    requests), including empty requests, pack and unpack with zero fill."""
+    log("[pack] batched, 3000 pairs")
+    rng = np.random.default_rng(12)
+    items, ref_dsts = [], []
+    for c in range(3):
+        lengths = [int(x) for x in rng.integers(0, 6, size=1000)]
+        S = 6
+        src = torch.from_numpy(rng.standard_normal((1000, S, 8)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+        cu = oracle.cu_seqlens_from_lengths(lengths)
+        cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+        dst = torch.zeros((int(cu[-1]), 8), dtype=torch.bfloat16, device=DEV)
+        items.append((src, cu_d, dst, None))
+        ref = oracle.pack_by_cu_seqlens(src.cpu().view(torch.int16).numpy(), cu)
+        ref_dsts.append((dst, ref, cu, src))
+    vl.pack_by_cu_seqlens_batched(items)
+    torch.cuda.synchronize()
+    for dst, ref, cu, src in ref_dsts:
+        assert np.array_equal(dst.cpu().view(torch.int16).numpy(), ref)
+    backs = []
+    for dst, ref, cu, src in ref_dsts:
+        backs.append(torch.full_like(src, 9.0))
+    vl.unpack_by_cu_seqlens_batched([(d, it[1], b, None) for (d, _, _, _), it, b in zip(ref_dsts, items, backs)])
+    torch.cuda.synchronize()
+    for (dst, ref, cu, src), b in zip(ref_dsts, backs):
+        exp = oracle.unpack_by_cu_seqlens(ref, cu, src.shape[1], zero_fill=True)
+        assert np.array_equal(b.cpu().view(torch.int16).numpy(), exp)
+
+
 # ------------------------------------------------------------------ tile schedule
 
 
