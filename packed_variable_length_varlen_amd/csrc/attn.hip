@@ -891,7 +891,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
     char* const vbuf[3] = {v0, v1, v2};
     const int p = p0 + I;
     if constexpr (((I - GR) & 1) == 0) {
+      // the MFMA wave wins issue arbitration on its SIMD during its phase
+      __builtin_amdgcn_s_setprio(2);
       if (wave_active) m_phase((p - GR) / 2, kbuf[(I / 2) % 3], vbuf[(I / 2 + 2) % 3]);
+      __builtin_amdgcn_s_setprio(0);
     } else {
       const char* src;
       int nb;
