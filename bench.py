@@ -255,6 +255,58 @@ def main():
     err(f"[bench] step {ms_per_step:.3f} ms, attention {attn_ms:.3f} ms = {achieved:.1f} TFLOP/s "
         f"({100 * achieved / BF16_PEAK_TFLOPS:.1f}% of bf16 peak); pairs {pairs}")
 
+    # Bandwidth-bound pieces in isolation: median / p10 / p90 of per-call event
+    # times, warm (calls back to back) and with the 256 MB last-level cache
+    # flushed before each call by reading a 512 MB buffer (a read leaves no
+    # dirty lines to be written back during the measured call).  All calls
+    # are enqueued before the one synchronisation, so no launch gap is timed.
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+
+    def call_stats(fn, flushed: bool, reps: int = 30, warm: int = 5):
+        for _ in range(warm):
+            fn()
+        pairs_ev = []
+        for _ in range(reps):
+            if flushed:
+                torch.sum(flush)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            pairs_ev.append((a, b))
+        torch.cuda.synchronize()
+        times = [a.elapsed_time(b) * 1e3 for a, b in pairs_ev]  # us
+        return [float(np.percentile(times, q)) for q in (50, 10, 90)]
+
+    def bw(nbytes, us):
+        return round(nbytes / us / 1e3, 1)  # GB/s
+
+    detail = {}
+    for name, fn, nbytes in (("pack", lambda: vl.pack_by_cu_seqlens_batched(pack_items), pack_bytes),
+                             ("unpack", lambda: vl.unpack_by_cu_seqlens_batched(unpack_items), unpack_bytes)):
+        rec = {"bytes": int(nbytes)}
+        for tag, fl in (("warm", False), ("flushed", True)):
+            med, p10, p90 = call_stats(fn, fl)
+            rec[tag] = {"us_median": round(med, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                        "GB/s": bw(nbytes, med), "pct_of_hbm": round(100 * nbytes / med / 1e3 / HBM_PEAK_GBS, 1)}
+        detail[name] = rec
+        err(f"[bench] {name}: warm {rec['warm']['pct_of_hbm']}% / flushed {rec['flushed']['pct_of_hbm']}% of HBM")
+    # block-local, one call per window type: % of MFMA peak as the metric asks,
+    # and % of HBM over its unique bytes (q, k, v read, out written) as the roofline
+    bl_bytes = 4 * bl_spec.B * bl_spec.n * bl_spec.H * bl_spec.D * 2
+    detail["block_local"] = []
+    for (lb, la), o, npairs in zip(bl_spec.windows, bouts, bl_pairs):
+        med, p10, p90 = call_stats(lambda: vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o),
+                                   True)
+        fl = 4.0 * bl_spec.D * bl_spec.H * npairs
+        detail["block_local"].append({"look_back": lb, "look_ahead": la, "us_median": round(med, 2),
+                                      "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                                      "TFLOP/s": round(fl / med / 1e6, 2),
+                                      "pct_of_bf16_peak": round(100 * fl / med / 1e6 / BF16_PEAK_TFLOPS, 3),
+                                      "pct_of_hbm_unique_bytes": round(100 * bl_bytes / med / 1e3 / HBM_PEAK_GBS, 1)})
+    err(f"[bench] block-local (flushed) us: {[d['us_median'] for d in detail['block_local']]}")
+
     cpu = None
     if not args.no_cpu_baseline:
         err("[bench] timing the CPU oracle on a bounded sample")
@@ -295,6 +347,7 @@ def main():
             "kernel_ms": round(attn_ms, 4),
         },
         "cpu_baseline": cpu,
+        "detail": detail,
     }
     print(json.dumps(line), flush=True)
 
