@@ -7,10 +7,15 @@
 // its own request (varlen), or the keys of its block window (block-local).
 //
 // Kernel design (ours; the pages only name library calls):
-//  * one work-group = 4 waves = 128 query rows of one (sequence, head); each
-//    wave owns 32 rows.  Q lives in registers for the whole key loop.
-//  * keys stream through LDS in tiles of BN rows, double-buffered: the next
-//    tile's global loads are in flight while the current one is consumed.
+//  * attn_bf16_pp_kernel (varlen, bf16): 8 waves = 256 query rows of one
+//    (request, head), two phase-shifted groups of four so that on each SIMD
+//    one wave issues MFMAs while the other does the softmax; K/V tiles rotate
+//    through three LDS buffers.  With the key split, split_merge_kernel
+//    combines the partial results of the last round's tiles.
+//  * attn_bf16_kernel (block-local, bf16) and attn_f32_kernel (fp32): 4
+//    waves = 128 query rows, keys double-buffered through LDS.
+//  * every wave owns 32 query rows; Q lives in registers for the whole key
+//    loop.
 //  * S^T = K Q^T on MFMA (bf16: v_mfma_f32_32x32x16_bf16; fp32:
 //    v_mfma_f32_32x32x2_f32), so each lane holds one query's scores for 16
 //    keys and the row max / row sum need one in-lane pass plus one lane-half
