@@ -173,8 +173,9 @@ def main():
     out_txt = torch.empty_like(slabs[0][0])
     out_img = torch.empty_like(slabs[0][1])
 
-    # partial results of the key split of the last round (allocated once)
-    workspace = torch.empty(max(vl.varlen_split_workspace_bytes(D), 1), dtype=torch.uint8, device=dev)
+    # workspace of the attention call (allocated once): staged V^T and the
+    # partial results of the key split of the last round
+    workspace = torch.empty(vl.varlen_split_workspace_bytes(T, R, H, D), dtype=torch.uint8, device=dev)
 
     bl_spec = wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"]
     bl = wl.make_block_local_inputs(bl_spec, torch.bfloat16)
@@ -343,7 +344,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_bf16_pp_kernel<128, 64> + split_merge_kernel<128, 256> (varlen_attn_fwd_split)",
+            "kernel": "vt_transpose_kernel<128> + attn_bf16_pp_kernel<128, 64, true> + "
+                      "split_merge_kernel<128, 256> (varlen_attn_fwd_split)",
             "kernel_ms": round(attn_ms, 4),
         },
         "cpu_baseline": cpu,

@@ -156,30 +156,40 @@ int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
                         int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale,
                         float* out, float* lse, vl_stream_t stream);
 
-/* varlen_attn_fwd_split: varlen_attn_fwd with the last, partial round of
- *   work-groups cut along the keys (same contract and results up to fp32
- *   summation order).  With `slots` work-groups resident at once on the
- *   device and T tiles of 128 query rows, tiles [0, full) run whole, full =
- *   T - T mod slots (0 if T < slots); when the remaining tail tiles would
- *   leave at least half of the slots idle, each is cut into
- *   parts = min(16, slots / tail, max_kv / 256) >= 2 key ranges of whole
- *   64-key tiles, run as separate work-groups that write unnormalised
- *   partial results to `workspace`; a second kernel on the same stream
- *   merges them (log-sum-exp weights) into out / lse.  Without such a tail
- *   the call is varlen_attn_fwd and `workspace` is not touched.
+/* varlen_attn_fwd_split: varlen_attn_fwd (same contract; results equal up to
+ *   fp32 summation order and the order of the keys inside each MFMA step)
+ *   with a caller-provided workspace that serves two purposes.
+ *   1. V^T staging: a first kernel writes V transposed, per head D rows of
+ *      vt_ld = roundup(kv_rows, 64) + 64 * num_reqs bf16 columns, request r's
+ *      keys from column 64 * (ceil(kv_cu_seqlens[r] / 64) + r), each request
+ *      padded with zeros to whole 64-key tiles; the attention kernel then
+ *      reads its V operands with plain 16-byte LDS reads.  This reads V once
+ *      and writes its copy once (HBM traffic of 2 x the V bytes).
+ *   2. Key split of the last round: with `slots` work-groups resident at
+ *      once on the device and T tiles of 256 query rows, tiles [0, full) run
+ *      whole, full = T - T mod slots (0 if T < slots); when the remaining
+ *      tail tiles would leave at least half of the slots idle, each is cut
+ *      into parts = min(16, slots / tail, max_kv / 256) >= 2 key ranges of
+ *      whole 64-key tiles, run as separate work-groups that write
+ *      unnormalised partial results to the workspace; a last kernel on the
+ *      same stream merges them (log-sum-exp weights) into out / lse.
+ *   kv_rows: rows of k and v (>= kv_cu_seqlens[num_reqs]; the Python binding
+ *   passes k.shape[0]); it sizes the V^T rows.
  *   workspace: device, 16-byte aligned, at least the bytes
- *   varlen_split_workspace_bytes reports for D; its contents need no
- *   initialisation and are scratch after the call.  Two calls that share a
- *   workspace must be ordered (same stream, or synchronised).  A missing or
- *   short workspace when a split is possible returns VL_EINVAL.
- * varlen_split_workspace_bytes: host-only; the workspace size for head size D
- *   on the current device (0 when no device can be queried).
+ *   varlen_split_workspace_bytes reports for (kv_rows, num_reqs, H, D); its
+ *   contents need no initialisation and are scratch after the call.  Two
+ *   calls that share a workspace must be ordered (same stream, or
+ *   synchronised).  A missing or short workspace returns VL_EINVAL; a V^T
+ *   row of more than 2^31 bytes (D * vt_ld * 2) returns VL_EUNSUPPORTED.
+ * varlen_split_workspace_bytes: host-only; the workspace size for these
+ *   sizes on the current device (the partial-result part is 0 when no device
+ *   can be queried).
  */
 int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
                           const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
-                          int32_t H, int32_t D, float scale, void* out, float* lse, void* workspace,
-                          int64_t workspace_bytes, vl_stream_t stream);
-int varlen_split_workspace_bytes(int32_t D, int64_t* bytes);
+                          int32_t H, int32_t D, float scale, void* out, float* lse, int64_t kv_rows,
+                          void* workspace, int64_t workspace_bytes, vl_stream_t stream);
+int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, int32_t D, int64_t* bytes);
 
 /* ---------------------------------------------------------------- block-local attention
  * block_local_attn_fwd: the block-local ("block-sparse") attention of the

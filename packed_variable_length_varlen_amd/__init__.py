@@ -50,8 +50,8 @@ _SIGNATURES = {
     "block_local_attn_fwd_f32": ([_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                   _c_i32, _c_f32, _vp, _vp, _vp], _c_int),
     "varlen_attn_fwd_split": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
-                               _vp, _vp, _vp, _c_i64, _vp], _c_int),
-    "varlen_split_workspace_bytes": ([_c_i32, _vp], _c_int),
+                               _vp, _vp, _c_i64, _vp, _c_i64, _vp], _c_int),
+    "varlen_split_workspace_bytes": ([_c_i64, _c_i32, _c_i32, _c_i32, _vp], _c_int),
     "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _vp, _vp, _vp],
                             _c_int),
     "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _c_i64, _vp],
@@ -317,22 +317,25 @@ def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(q_cu), _ptr(kv_cu), int(max_q), int(max_kv), R, H, D, float(scale),
             _ptr(out), _ptr(lse)]
     if fn_name == "varlen_attn_fwd_split":
-        need = varlen_split_workspace_bytes(D)
+        kv_rows = k.shape[0]
+        need = varlen_split_workspace_bytes(kv_rows, R, H, D)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
             if stream is not None and stream != torch.cuda.current_stream(q.device):
                 workspace.record_stream(stream)
         _gpu(workspace, "workspace")
-        args += [_ptr(workspace), workspace.numel() * workspace.element_size()]
+        args += [kv_rows, _ptr(workspace), workspace.numel() * workspace.element_size()]
     rc = getattr(load_library(), fn_name)(*args, _stream(stream))
     _check(rc, fn_name)
     return (out, lse) if return_lse else out
 
 
-def varlen_split_workspace_bytes(D: int) -> int:
-    """Workspace bytes varlen_attn_fwd_split needs for head size D on the current device."""
+def varlen_split_workspace_bytes(kv_rows: int, num_reqs: int, H: int, D: int) -> int:
+    """Workspace bytes varlen_attn_fwd_split needs on the current device for K/V
+    of kv_rows rows in num_reqs requests, H heads of size D."""
     n = ctypes.c_int64()
-    _check(load_library().varlen_split_workspace_bytes(int(D), ctypes.byref(n)), "varlen_split_workspace_bytes")
+    _check(load_library().varlen_split_workspace_bytes(int(kv_rows), int(num_reqs), int(H), int(D),
+                                                       ctypes.byref(n)), "varlen_split_workspace_bytes")
     return n.value
 
 
@@ -347,9 +350,10 @@ def varlen_attn_fwd(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=N
 def varlen_attn_fwd_split(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
                           lse=None, workspace: Optional[torch.Tensor] = None, padded_tokens: int = 0,
                           attn_mask=None, return_lse: bool = False, stream=None):
-    """varlen_attn_fwd with the last partial round cut along the keys; `workspace`
-    (a device buffer of varlen_split_workspace_bytes(D) bytes) is allocated
-    when not given."""
+    """varlen_attn_fwd through a workspace: V is staged transposed there, and
+    the last partial round is cut along the keys.  `workspace` (a device
+    buffer of varlen_split_workspace_bytes(k.shape[0], num_reqs, H, D) bytes)
+    is allocated when not given."""
     return _varlen("varlen_attn_fwd_split", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
                    max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace)
 

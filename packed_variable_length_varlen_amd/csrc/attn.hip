@@ -62,6 +62,10 @@ struct AttnArgs {
   int slots;
   int max_kv;
   float* ws;
+  // V^T staged for the workspace launch: [H][D][vt_ld] bf16, request r's
+  // keys from column vt_col_base(kv_cu[r], r) (nullptr: read V directly)
+  void* vt;
+  int64_t vt_ld;
 };
 
 // ---------------------------------------------------------------- tile setup
@@ -73,6 +77,7 @@ struct TileRange {
   int k_lo, k_hi;  // keys of the tile, relative to kv_base
   int seq_q0;   // row of q0 inside its sequence (block-local windows)
   int unit;     // partial-result slot of a split work item, -1 for a whole tile
+  int req;      // request (varlen) or batch row (block-local)
   bool valid;
 };
 
@@ -91,6 +96,7 @@ __device__ __forceinline__ TileRange tile_range(const AttnArgs& a) {
     const int qs = a.q_cu[w.req];
     const int qe = a.q_cu[w.req + 1];
     t.h = w.head;
+    t.req = w.req;
     t.q0 = qs + w.qt * BM;
     t.q1 = min(qe, t.q0 + BM);
     t.kv_base = a.kv_cu[w.req];
@@ -111,6 +117,7 @@ __device__ __forceinline__ TileRange tile_range(const AttnArgs& a) {
     const int bh = id / a.nqt;
     t.h = bh % a.H;
     const int b = bh / a.H;
+    t.req = b;
     const int i0 = qt * BM;
     const int i1 = min(a.n, i0 + BM);
     t.q0 = b * a.n + i0;
@@ -234,6 +241,9 @@ template <int CPR>
 __device__ __forceinline__ int k_swz(int r) { return r & (CPR - 1); }
 template <int CPR>
 __device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) & (CPR - 1); }
+//  V^T (rows of 64 keys = 128 bytes, two rows per 256-byte bank line): the
+//  16 rows a wave reads together get distinct 16-byte bank groups.
+__device__ __forceinline__ int vt_swz(int r) { return (r >> 1) & 7; }
 
 // Copies N wave-wide 16-byte-per-lane rows of a tile straight into LDS
 // (buffer_load ... lds): load i lands at lds + i KB, lane l at +16*l; lane l
@@ -683,9 +693,16 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // are complete for phase 2j+2, where group 0 first reads them.  The phase
 // loop is unrolled six times so every LDS access names one __shared__ array
 // and the compiler's LDS-copy waits stay precise.
-template <int D, int BN>
+// kVt: V tiles come from the staged V^T (a.vt) as D rows of BN keys, so the
+// V^T operands are plain 16-byte LDS reads instead of transposing 8-byte
+// reads (which move half as many bytes per LDS cycle and need their
+// addresses computed on the VALU).
+template <int D, int BN, bool kVt>
 __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   using G = Bf16Geo<D, 8, BN>;
+  static_assert(!kVt || BN == kVtTile, "V^T tiles are whole padded 64-key groups");
+  constexpr int VROW = BN * 2;       // bytes per V^T row (one tile's keys of one feature)
+  constexpr int VRPI = 1024 / VROW;  // V^T rows per wave-wide 16-byte load
   constexpr int BM = 256;
   constexpr int L = G::kLoadsPerWave;
   __shared__ __attribute__((aligned(16))) char k0[G::kTileBytes];
@@ -725,12 +742,19 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   const int ld_pchunk = lane % G::CPR;
   const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
   // Prologue copies: all 8 waves, L loads each per tile.
+  // V^T copies: lane l of load i lands on feature row i*VRPI + l/8 at
+  // physical chunk l%8 and fetches logical chunk (l%8) ^ vt_swz(row).
+  const uint32_t vt_rs = (uint32_t)(a.vt_ld * 2);
+  auto vt_off = [&](int load) {
+    const int row = load * VRPI + lane / 8;
+    return (uint32_t)row * vt_rs + (((lane & 7) ^ vt_swz(row)) * 16);
+  };
   uint32_t ld_koff[L], ld_voff[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const int row = (L * wave + i) * G::RPI + ld_row_in_blk;
     ld_koff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ k_swz<G::CPR>(row)) * 16;
-    ld_voff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(row)) * 16;
+    ld_voff[i] = kVt ? vt_off(L * wave + i) : (uint32_t)row * rs_bytes + (ld_pchunk ^ v_swz<G::CPR>(row)) * 16;
   }
   // Loop copies: the four waves of one group move a whole tile, 2L loads each;
   // group 1 copies K (rows by K swizzle), group 0 copies V.
@@ -741,25 +765,33 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   for (int i = 0; i < L2; ++i) {
     const int row = (L2 * gw + i) * G::RPI + ld_row_in_blk;
     const int swz = grp == 1 ? k_swz<G::CPR>(row) : v_swz<G::CPR>(row);
-    ld_goff[i] = (uint32_t)row * rs_bytes + (ld_pchunk ^ swz) * 16;
+    ld_goff[i] = (kVt && grp == 0) ? vt_off(L2 * gw + i) : (uint32_t)row * rs_bytes + (ld_pchunk ^ swz) * 16;
   }
   const char* kbase = (const char*)a.k + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
-  const char* vbase = (const char*)a.v + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
+  const char* vbase =
+      kVt ? (const char*)a.vt + ((int64_t)h * D * a.vt_ld + vt_col_base(tr.kv_base, tr.req)) * 2
+          : (const char*)a.v + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
   const int nkeys = tr.k_hi - tr.k_lo;
   const int ntiles = (nkeys + BN - 1) / BN;
   const bool ragged = (nkeys % BN) != 0;
   // Source and byte count of tile `tile`; past the last tile a zero-byte
   // descriptor reads nothing (the copy still issues, keeping wait counts uniform).
-  auto tile_src = [&](const char* base, int tile, const char*& src, int& nb) {
+  // A V^T tile is D whole rows of BN keys (zero-filled past the request).
+  auto tile_src = [&](const char* base, bool is_vt, int tile, const char*& src, int& nb) {
     const bool ok = tile < ntiles;
-    src = ok ? base + (int64_t)(tr.k_lo + tile * BN) * rs_bytes : base;
-    nb = ok ? (min(BN, nkeys - tile * BN) - 1) * (int)rs_bytes + G::ROW : 0;
+    if (is_vt) {
+      src = ok ? base + (int64_t)(tr.k_lo + tile * BN) * 2 : base;
+      nb = ok ? (D - 1) * (int)vt_rs + VROW : 0;
+    } else {
+      src = ok ? base + (int64_t)(tr.k_lo + tile * BN) * rs_bytes : base;
+      nb = ok ? (min(BN, nkeys - tile * BN) - 1) * (int)rs_bytes + G::ROW : 0;
+    }
   };
   // Tile `tile` of K or V into dst, this wave's share of an all-wave copy.
-  auto copy_tile = [&](const char* base, int tile, char* dst, const uint32_t(&off)[L]) {
-    const bool ok = tile < ntiles;
-    const char* src = ok ? base + (int64_t)(tr.k_lo + tile * BN) * rs_bytes : base;
-    const int nb = ok ? (min(BN, nkeys - tile * BN) - 1) * (int)rs_bytes + G::ROW : 0;
+  auto copy_tile = [&](const char* base, bool is_vt, int tile, char* dst, const uint32_t(&off)[L]) {
+    const char* src;
+    int nb;
+    tile_src(base, is_vt, tile, src, nb);
 #pragma unroll
     for (int i = 0; i < L; ++i) lds_dma_one(src, nb, dst + (L * wave + i) * 1024, off[i]);
   };
@@ -778,6 +810,12 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
     const int chunk = (byte_in_row >> 4) ^ v_swz<G::CPR>(v_row);
     v_rd[db] = v_row * G::ROW + chunk * 16 + (byte_in_row & 15);
   }
+  //  V^T operand from a V^T tile: lane (ql, g), step (kc, db) reads logical
+  //  chunk 2kc+g (stored keys 16kc + 8g .. +7, in P's k-slot order) of
+  //  feature row db*32 + ql.
+  int vt_rd[G::NKC];
+#pragma unroll
+  for (int kc = 0; kc < G::NKC; ++kc) vt_rd[kc] = ql * VROW + (((2 * kc + g) ^ vt_swz(ql)) * 16);
 
   RowState<G::NKB, G::NDB> st;
   st.init();
@@ -790,10 +828,14 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
       constexpr int VPF = 6;
       constexpr int NSTEP = G::NKC * G::NDB;
       auto read_v = [&](int step) {
-        const char* p = vl + (step / G::NDB) * 16 * G::ROW + v_rd[step % G::NDB];
-        const i16x4 lo4 = lds_read_tr(p);
-        const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (kVt) {
+          return *(const bf16x8*)(vl + (step % G::NDB) * 32 * VROW + vt_rd[step / G::NDB]);
+        } else {
+          const char* p = vl + (step / G::NDB) * 16 * G::ROW + v_rd[step % G::NDB];
+          const i16x4 lo4 = lds_read_tr(p);
+          const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       };
       bf16x8 va[VPF + 1];
 #pragma unroll
@@ -905,10 +947,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
       int nb;
       char* dst;
       if constexpr ((I & 1) == 0) {
-        tile_src(kbase, p / 2 + 2, src, nb);
+        tile_src(kbase, false, p / 2 + 2, src, nb);
         dst = kbuf[(I / 2 + 2) % 3];
       } else {
-        tile_src(vbase, p / 2 + 1, src, nb);
+        tile_src(vbase, kVt, p / 2 + 1, src, nb);
         dst = vbuf[(I / 2 + 1) % 3];
       }
       v_phase((p - GR - 1) / 2, [&](int i) { lds_dma_one(src, nb, dst + (L2 * gw + i) * 1024, ld_goff[i]); });
@@ -939,9 +981,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
     }
   };
 
-  copy_tile(kbase, 0, k0, ld_koff);
-  copy_tile(kbase, 1, k1, ld_koff);
-  copy_tile(vbase, 0, v0, ld_voff);
+  copy_tile(kbase, false, 0, k0, ld_koff);
+  copy_tile(kbase, false, 1, k1, ld_koff);
+  copy_tile(vbase, kVt, 0, v0, ld_voff);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   wg_barrier();
   if (grp == 0)
@@ -1159,6 +1201,70 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
 // m = max m_p, w_p = 2^(m_p - m), out = sum_p w_p O_p / sum_p w_p l_p,
 // lse = (m + log2 sum_p w_p l_p) ln 2 -- taken in one pass over the parts with
 // a running maximum.  Empty parts carry m_p = -inf, l_p = 0 and are skipped.
+// ---------------------------------------------------------------- V^T staging
+
+// One 64-key tile of one head of V -> V^T: V rows [T, H, D] (bf16) of request
+// r's keys key0 .. key0+63 become D rows of 64 columns at
+// vt_col_base(kv_cu[r], r) + key0, each 16-key group stored in the P k-slot
+// order (vt_pos_of_key), keys past the request zero.  Block b covers column
+// tile b mod (vt_ld / 64) of head b / (vt_ld / 64); tiles in the gaps between
+// requests are never read and are skipped.  Through LDS so that both the V
+// reads (16 lanes per 256-byte row) and the V^T writes (8 lanes per 128-byte
+// row) are whole-line accesses.
+template <int D>
+__global__ void __launch_bounds__(256) vt_transpose_kernel(AttnArgs a) {
+  constexpr int LD = D + 2;  // bf16 per LDS row: an odd dword count, so column reads spread over banks
+  constexpr int CPR = D / 8;
+  __shared__ uint32_t sm[kVtTile * LD / 2];
+  const int ntc = (int)(a.vt_ld / kVtTile);
+  const int h = blockIdx.x / ntc;
+  const int64_t col0 = (int64_t)(blockIdx.x % ntc) * kVtTile;
+  // request of the tile: the last r whose first column is <= col0
+  int lo = 0, hi = a.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (vt_col_base(a.kv_cu[mid], mid) <= col0)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int kv0 = a.kv_cu[lo];
+  const int len = a.kv_cu[lo + 1] - kv0;
+  const int64_t key0 = col0 - vt_col_base(kv0, lo);
+  if (key0 < 0 || key0 >= len) return;
+  const int valid = min(kVtTile, len - (int)key0);
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = t; i < kVtTile * CPR; i += 256) {
+    const int k = i / CPR, ch = i % CPR;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (k < valid)
+      x = *(const uint4*)((const __bf16*)a.v + ((int64_t)(kv0 + key0 + k) * a.H + h) * D + ch * 8);
+    uint32_t* d = sm + (k * LD + ch * 8) / 2;
+    d[0] = x.x;
+    d[1] = x.y;
+    d[2] = x.z;
+    d[3] = x.w;
+  }
+  __syncthreads();
+  const uint16_t* sh = (const uint16_t*)sm;
+#pragma unroll
+  for (int i = t; i < D * 8; i += 256) {
+    const int d = i / 8, cc = i % 8;  // feature row, 16-byte chunk (stored positions 8cc .. 8cc+7)
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      // stored position p holds key 4 (p / 8) + (p mod 4) + 8 ((p / 4) mod 2) of its group of 16
+      const int p0 = (8 * cc + j) & 15, p1 = (8 * cc + j + 1) & 15;
+      const int base = 16 * (cc >> 1);
+      const int k0 = base + 4 * (p0 >> 3) + (p0 & 3) + 8 * ((p0 >> 2) & 1);
+      const int k1 = base + 4 * (p1 >> 3) + (p1 & 3) + 8 * ((p1 >> 2) & 1);
+      w[j / 2] = (uint32_t)sh[k0 * LD + d] | ((uint32_t)sh[k1 * LD + d] << 16);
+    }
+    *(uint4*)((__bf16*)a.vt + ((int64_t)h * D + d) * a.vt_ld + col0 + cc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <int D, int BM>
 __global__ void __launch_bounds__(256) split_merge_kernel(AttnArgs a) {
   constexpr int C4 = D / 4;         // 4-float groups per row
@@ -1238,7 +1344,7 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 template <int D>
 constexpr auto bf16_varlen_kernel() {
-  return &vl::attn_bf16_pp_kernel<D, kBf16VarlenBN>;
+  return &vl::attn_bf16_pp_kernel<D, kBf16VarlenBN, true>;
 }
 
 // Work-groups of the bf16 varlen kernel resident at once on the current
@@ -1288,10 +1394,14 @@ inline VarlenPlan varlen_plan(bool f32, bool split, int64_t num_reqs, int64_t ma
   return p;
 }
 
-// Bytes of partial results a split launch may write: per slot, BM rows of D
-// floats and BM (offset, sum) float pairs.
-inline int64_t split_workspace_bytes(int slots, int D) {
-  return (int64_t)slots * kBf16VarlenBM * ((int64_t)D * 4 + 8);
+// Workspace of the split launch: the partial results the key split may
+// write (per slot, BM rows of D floats and BM (offset, sum) float pairs),
+// rounded up to 256 bytes, then V^T ([H][D][vt_ld] bf16).
+inline int64_t split_partial_bytes(int slots, int D) {
+  return ((int64_t)slots * kBf16VarlenBM * ((int64_t)D * 4 + 8) + 255) / 256 * 256;
+}
+inline int64_t split_workspace_bytes(int slots, int64_t kv_rows, int64_t num_reqs, int64_t H, int D) {
+  return split_partial_bytes(slots, D) + H * D * vl::vt_row_len(kv_rows, num_reqs) * 2;
 }
 
 int launch_status() {
@@ -1301,9 +1411,9 @@ int launch_status() {
 template <bool kF32>
 int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_cu,
                   const int32_t* kv_cu, int32_t max_q, int32_t max_kv, int32_t num_reqs,
-                  int32_t H, int32_t D, float scale, void* out, float* lse, bool split, void* workspace,
-                  int64_t workspace_bytes, hipStream_t stream) {
-  if (num_reqs < 0 || max_q < 0 || max_kv < 0 || H < 1) return VL_EINVAL;
+                  int32_t H, int32_t D, float scale, void* out, float* lse, bool split, int64_t kv_rows,
+                  void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (num_reqs < 0 || max_q < 0 || max_kv < 0 || H < 1 || kv_rows < 0) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
   if (num_reqs == 0 || max_q == 0) return VL_OK;
   if (!q || !k || !v || !q_cu || !kv_cu || !out) return VL_EINVAL;
@@ -1312,8 +1422,11 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   const VarlenPlan plan = varlen_plan(kF32, split, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
-  if (plan.slots > 0 &&
-      (!workspace || !aligned16(workspace) || workspace_bytes < split_workspace_bytes(plan.slots, D)))
+  // the split launch stages V^T; its copies address a head's V^T with 32-bit offsets
+  const int64_t vt_ld = split ? vl::vt_row_len(kv_rows, num_reqs) : 0;
+  if (split && ((int64_t)D * vt_ld * 2 > INT32_MAX || vt_ld / vl::kVtTile * H > INT32_MAX)) return VL_EUNSUPPORTED;
+  if (split && (!workspace || !aligned16(workspace) ||
+                workspace_bytes < split_workspace_bytes(plan.slots, kv_rows, num_reqs, H, D)))
     return VL_EINVAL;
   vl::AttnArgs a{};
   a.q = q;
@@ -1330,6 +1443,10 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   a.slots = plan.slots;
   a.max_kv = max_kv;
   a.ws = (float*)workspace;
+  if (split) {
+    a.vt = (char*)workspace + split_partial_bytes(plan.slots, D);
+    a.vt_ld = vt_ld;
+  }
   (void)hipGetLastError();
   if (kF32) {
     if (D == 128)
@@ -1338,12 +1455,24 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
     return launch_status();
   }
-  if (D == 128)
-    hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<128, kBf16VarlenBN>), dim3((unsigned)G), dim3(plan.threads), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<64, kBf16VarlenBN>), dim3((unsigned)G), dim3(plan.threads), 0,
-                       stream, a);
+  if (split) {
+    const unsigned tb = (unsigned)(vt_ld / vl::kVtTile * H);
+    if (D == 128) {
+      hipLaunchKernelGGL((vl::vt_transpose_kernel<128>), dim3(tb), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<128, kBf16VarlenBN, true>), dim3((unsigned)G),
+                         dim3(plan.threads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((vl::vt_transpose_kernel<64>), dim3(tb), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<64, kBf16VarlenBN, true>), dim3((unsigned)G),
+                         dim3(plan.threads), 0, stream, a);
+    }
+  } else if (D == 128) {
+    hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<128, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<64, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads),
+                       0, stream, a);
+  }
   if (plan.slots > 0) {
     // BM / (256 / (D/4)) blocks per possible tail tile (there are fewer than
     // slots of them); blocks past the tail return at once
@@ -1407,21 +1536,21 @@ int varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
                     const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
                     int32_t H, int32_t D, float scale, void* out, float* lse, vl_stream_t stream) {
   return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
-                              scale, out, lse, false, nullptr, 0, (hipStream_t)stream);
+                              scale, out, lse, false, 0, nullptr, 0, (hipStream_t)stream);
 }
 
 int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
                           const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
-                          int32_t H, int32_t D, float scale, void* out, float* lse, void* workspace,
-                          int64_t workspace_bytes, vl_stream_t stream) {
+                          int32_t H, int32_t D, float scale, void* out, float* lse, int64_t kv_rows,
+                          void* workspace, int64_t workspace_bytes, vl_stream_t stream) {
   return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
-                              scale, out, lse, true, workspace, workspace_bytes, (hipStream_t)stream);
+                              scale, out, lse, true, kv_rows, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
-int varlen_split_workspace_bytes(int32_t D, int64_t* bytes) {
-  if (!bytes) return VL_EINVAL;
+int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, int32_t D, int64_t* bytes) {
+  if (!bytes || kv_rows < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
-  *bytes = split_workspace_bytes(bf16_varlen_slots(D), D);
+  *bytes = split_workspace_bytes(bf16_varlen_slots(D), kv_rows, num_reqs, H, D);
   return VL_OK;
 }
 
@@ -1430,7 +1559,7 @@ int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
                         int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale,
                         float* out, float* lse, vl_stream_t stream) {
   return varlen_common<true>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
-                             scale, out, lse, false, nullptr, 0, (hipStream_t)stream);
+                             scale, out, lse, false, 0, nullptr, 0, (hipStream_t)stream);
 }
 
 int block_local_attn_fwd(const void* q, const void* k, const void* v, int32_t B, int32_t n,

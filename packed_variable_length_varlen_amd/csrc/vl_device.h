@@ -224,4 +224,19 @@ inline int64_t grid_blocks(int64_t num_reqs, int64_t max_q, int64_t H, int64_t b
   return ((upper + group - 1) / group) * group;
 }
 
+// Transposed V (V^T) staged by the workspace launch: per head, D rows of
+// vt_ld bf16 columns.  Request r's keys start at column
+// 64 * (ceil(kv_cu[r] / 64) + r): a multiple of 64, and at least
+// roundup(len_r, 64) columns past request r-1's start, so every request owns
+// whole 64-key tiles and no tile overlaps another request's.
+constexpr int kVtTile = 64;
+__host__ __device__ inline int64_t vt_col_base(int kv_start, int r) {
+  return (int64_t)kVtTile * ((kv_start + kVtTile - 1) / kVtTile + r);
+}
+// Columns per V^T row for kv_rows key rows in num_reqs requests: bounds
+// vt_col_base(kv_cu[R-1], R-1) + roundup(len, 64) for any cu_seqlens within kv_rows.
+inline int64_t vt_row_len(int64_t kv_rows, int64_t num_reqs) {
+  return (kv_rows + kVtTile - 1) / kVtTile * kVtTile + kVtTile * num_reqs;
+}
+
 }  // namespace vl

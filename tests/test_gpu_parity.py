@@ -442,18 +442,40 @@ def test_varlen_split_workspace_checked():
     ql = [3000]
     q, k, v = wl.random_varlen_case(47, ql, 1, 128, torch.bfloat16)
     cu = torch.tensor([0, 3000], dtype=torch.int32, device=DEV)
-    need = vl.varlen_split_workspace_bytes(128)
+    need = vl.varlen_split_workspace_bytes(3000, 1, 1, 128)
     assert need > 0
     short = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(vl.VarlenError):
         vl.varlen_attn_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), cu, cu, 3000, 3000, workspace=short)
-    # no split possible (max_kv < 512): the workspace is not needed
-    small = [100]
-    q2, k2, v2 = wl.random_varlen_case(48, small, 1, 128, torch.bfloat16)
-    cu2 = torch.tensor([0, 100], dtype=torch.int32, device=DEV)
-    o_split = vl.varlen_attn_fwd_split(q2.to(DEV), k2.to(DEV), v2.to(DEV), cu2, cu2, 100, 100, workspace=short)
-    o_plain = vl.varlen_attn_fwd(q2.to(DEV), k2.to(DEV), v2.to(DEV), cu2, cu2, 100, 100)
-    assert torch.equal(o_split, o_plain)
+    exact = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o_split = vl.varlen_attn_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), cu, cu, 3000, 3000, workspace=exact)
+    ro, _ = oracle.varlen_attention(to64(q), to64(k), to64(v), [0, 3000], [0, 3000], wl.softmax_scale(128),
+                                    rows=np.arange(0, 3000, 7))
+    check_close(to64(o_split)[::7], ro, False, "exact workspace")
+
+
+# (lengths, kv lengths or None, heads, head size): no key split (max_kv < 512),
+# ragged tails, empty requests, many requests (gaps between their V^T columns)
+VT_CASES = [
+    ([300], None, 2, 128),
+    ([17, 64, 129, 1, 0, 255], None, 3, 128),
+    ([40, 90, 7], [130, 0, 511], 2, 64),
+    ([5] * 100, [33] * 100, 1, 128),
+]
+
+
+@pytest.mark.parametrize("ql,kl,H,D", VT_CASES)
+def test_varlen_staged_vt_equals_direct_v(ql, kl, H, D):
+    """The workspace launch reads V through the staged V^T; without a key
+    split it feeds the MFMAs exactly the operands the direct launch reads, so
+    out and lse are the same bits."""
+    kl = kl or ql
+    log(f"[varlen] staged V^T vs direct V: R={len(ql)} H={H} D={D}")
+    q, k, v = wl.random_varlen_case(51, ql, H, D, torch.bfloat16, kv_lengths=kl)
+    q_cu, kv_cu = oracle.cu_seqlens_from_lengths(ql), oracle.cu_seqlens_from_lengths(kl)
+    o1, l1 = _run_varlen(q, k, v, q_cu, kv_cu, wl.softmax_scale(D), False, split=True)
+    o2, l2 = _run_varlen(q, k, v, q_cu, kv_cu, wl.softmax_scale(D), False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def _pipeline(inp):

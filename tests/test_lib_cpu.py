@@ -90,11 +90,20 @@ def test_bad_scalars_rejected_before_launch(lib):
     assert lib.joint_cu_seqlens(p, -1, p, 2, p, p, p, p, None) == VL_EINVAL
     # tile map: output too small
     assert lib.varlen_tile_map(p, p, 300, 300, 4, 2, 128, 0, 0, p, 1, None) == VL_EINVAL
-    # split entry point: same scalar checks as the plain one
-    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 96, 0.1, p, None, p, 0, None) == VL_EUNSUPPORTED
-    assert lib.varlen_attn_fwd_split(p, p, p, p, p, -1, 8, 1, 2, 64, 0.1, p, None, p, 0, None) == VL_EINVAL
-    assert lib.varlen_split_workspace_bytes(96, p) == VL_EUNSUPPORTED
-    assert lib.varlen_split_workspace_bytes(64, None) == VL_EINVAL
+    # split entry point: same scalar checks as the plain one, plus its
+    # workspace (short -> EINVAL) and the 32-bit V^T row limit, all before any launch
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 96, 0.1, p, None, 8, p, 1 << 20, None) \
+        == VL_EUNSUPPORTED
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, -1, 8, 1, 2, 64, 0.1, p, None, 8, p, 1 << 20, None) == VL_EINVAL
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, -1, p, 1 << 20, None) == VL_EINVAL
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, 8, p, 16, None) == VL_EINVAL
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, 8, None, 1 << 20, None) \
+        == VL_EINVAL
+    assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 128, 0.1, p, None, 9_000_000, p, 1 << 40, None) \
+        == VL_EUNSUPPORTED
+    assert lib.varlen_split_workspace_bytes(8, 1, 2, 96, p) == VL_EUNSUPPORTED
+    assert lib.varlen_split_workspace_bytes(8, 1, 2, 64, None) == VL_EINVAL
+    assert lib.varlen_split_workspace_bytes(-1, 1, 2, 64, p) == VL_EINVAL
 
 
 @pytest.mark.parametrize("split", [False, True])
@@ -107,6 +116,18 @@ def test_launch_shape_matches_schedule_spec(lib, max_q, R, H, D, split):
     expect = oracle.grid_blocks(R, max_q, H, bm, chunk, slots=slots) if max_q > 0 and R > 0 else 0
     assert G == expect
     assert G % (8 * chunk) == 0
+
+
+@pytest.mark.parametrize("kv_rows,R,H,D", [(0, 1, 1, 64), (100, 3, 2, 64), (16640, 1, 24, 128),
+                                           (131592, 4, 24, 128), (64, 1000, 2, 128)])
+def test_split_workspace_size_is_the_documented_layout(lib, kv_rows, R, H, D):
+    """Partial results of the key split (slots x 256 rows x (D floats + 2
+    floats), rounded up to 256 bytes), then V^T: H x D rows of
+    roundup(kv_rows, 64) + 64 R bf16 columns."""
+    _, _, _, slots = vl.varlen_launch_shape(4096, 1, 1, D, max_kv=4096, split=True)
+    partial = -(-(slots * 256 * (D * 4 + 8)) // 256) * 256
+    vt_ld = -(-kv_rows // 64) * 64 + 64 * R
+    assert vl.varlen_split_workspace_bytes(kv_rows, R, H, D) == partial + H * D * vt_ld * 2
 
 
 def test_mixfusion_plan_native_matches_oracle_and_pages(lib):
