@@ -274,6 +274,22 @@ __device__ __forceinline__ void lds_dma_one(const char* base, int nbytes, char* 
 #endif
 }
 
+// As lds_dma_one with the copy's LDS destination and source both advanced by
+// the immediate IMM: copies of one wave into consecutive 1 KB pieces can share
+// one LDS base (one M0 value) and pass voff - IMM.  The hardware range check
+// covers voffset + IMM.
+template <int IMM>
+__device__ __forceinline__ void lds_dma_imm(const char* base, int nbytes, char* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t b = (uint64_t)base;
+  const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+  const int un = __builtin_amdgcn_readfirstlane(nbytes);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)ub, 0, un, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, IMM, 0);
+#endif
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -760,6 +776,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   // group 1 copies K (rows by K swizzle), group 0 copies V.
   constexpr int L2 = 2 * L;
   const int gw = wave & 3;
+  // (ld_goff[i] >= 1024 i: load i starts at row >= i * 1024 / row bytes, and
+  // every source row is at least that many bytes apart)
   uint32_t ld_goff[L2];
 #pragma unroll
   for (int i = 0; i < L2; ++i) {
@@ -953,7 +971,17 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
         tile_src(vbase, kVt, p / 2 + 1, src, nb);
         dst = vbuf[(I / 2 + 1) % 3];
       }
-      v_phase((p - GR - 1) / 2, [&](int i) { lds_dma_one(src, nb, dst + (L2 * gw + i) * 1024, ld_goff[i]); });
+      // the wave's L2 copies share one LDS base; load i adds i KB as an immediate
+      char* const wdst = dst + L2 * gw * 1024;
+      v_phase((p - GR - 1) / 2, [&](int i) {
+        static_assert(L2 <= 4, "immediate offsets up to 3 KB");
+        switch (i) {
+          case 0: lds_dma_imm<0>(src, nb, wdst, ld_goff[0]); break;
+          case 1: lds_dma_imm<1024>(src, nb, wdst, ld_goff[1] - 1024); break;
+          case 2: lds_dma_imm<2048>(src, nb, wdst, ld_goff[L2 > 2 ? 2 : 0] - 2048); break;
+          default: lds_dma_imm<3072>(src, nb, wdst, ld_goff[L2 > 3 ? 3 : 0] - 3072); break;
+        }
+      });
       __builtin_amdgcn_s_waitcnt(kWaitVm0 | L2);
     }
     wg_barrier();
