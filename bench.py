@@ -307,6 +307,28 @@ def main():
                                       "pct_of_bf16_peak": round(100 * fl / med / 1e6 / BF16_PEAK_TFLOPS, 3),
                                       "pct_of_hbm_unique_bytes": round(100 * bl_bytes / med / 1e3 / HBM_PEAK_GBS, 1)})
     err(f"[bench] block-local (flushed) us: {[d['us_median'] for d in detail['block_local']]}")
+    # block-local at the DiT vocoder's production shape: CFG as batch 2, 4000
+    # frames (167 blocks, the last of 16), own-block and one-neighbour windows,
+    # in the pages' fp32 and in bf16
+    prod_n, prod_b = 4000, 2
+    detail["block_local_production"] = []
+    for pdt in (torch.float32, torch.bfloat16):
+        pin = wl.make_block_local_inputs(bl_spec, pdt, n=prod_n, B=prod_b, seed=prod_n)
+        pq, pk, pv = pin.q.to(dev), pin.k.to(dev), pin.v.to(dev)
+        po = torch.empty_like(pq)
+        fn = vl.block_local_attn_fwd_f32 if pdt == torch.float32 else vl.block_local_attn_fwd
+        pbytes = 4 * prod_b * prod_n * bl_spec.H * bl_spec.D * pq.element_size()
+        for lb, la in ((0, 0), (1, 0), (0, 1)):
+            med, p10, p90 = call_stats(lambda: fn(pq, pk, pv, bl_spec.block, lb, la, pin.scale, out=po), True)
+            fl = 4.0 * bl_spec.D * bl_spec.H * prod_b * block_local_pairs(prod_n, bl_spec.block, lb, la)
+            detail["block_local_production"].append({
+                "dtype": "f32" if pdt == torch.float32 else "bf16", "B": prod_b, "n": prod_n,
+                "look_back": lb, "look_ahead": la, "us_median": round(med, 2), "us_p10": round(p10, 2),
+                "us_p90": round(p90, 2), "TFLOP/s": round(fl / med / 1e6, 2),
+                "pct_of_hbm_unique_bytes": round(100 * pbytes / med / 1e3 / HBM_PEAK_GBS, 1)})
+        del pq, pk, pv, po, pin
+    err(f"[bench] block-local production (flushed) us: "
+        f"{[(d['dtype'], d['look_back'], d['look_ahead'], d['us_median']) for d in detail['block_local_production']]}")
 
     cpu = None
     if not args.no_cpu_baseline:
