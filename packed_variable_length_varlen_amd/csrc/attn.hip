@@ -855,6 +855,11 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       };
+      // P(k-1) is still in s as fp32: add its row sums a few per MFMA, where
+      // this wave's VALU slots are otherwise idle (S(k) overwrites s only after).
+      constexpr int kSumPerStep = G::NKB * 16 / NSTEP;
+      static_assert(kSumPerStep * NSTEP == G::NKB * 16, "whole scores per PV step");
+      float ls0 = 0.f, ls1 = 0.f;
       bf16x8 va[VPF + 1];
 #pragma unroll
       for (int step = 0; step < VPF; ++step) va[step] = read_v(step);
@@ -864,8 +869,20 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
         VL_SCHED_BARRIER(0);
         st.o[step % G::NDB] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[step / G::NDB], st.o[step % G::NDB], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < kSumPerStep; ++t) {
+          const int idx = step * kSumPerStep + t;
+          if (t & 1)
+            ls1 += s[idx >> 4][idx & 15];
+          else
+            ls0 += s[idx >> 4][idx & 15];
+        }
+        // an opaque use keeps the adds in this step (they would otherwise
+        // sink to the sums' only use after the loop)
+        asm volatile("" : "+v"(ls0), "+v"(ls1));
         VL_SCHED_BARRIER(0);
       }
+      st.l += ls0 + ls1;
     }
     if (k < ntiles) {
       constexpr int KPF = 3;
@@ -922,25 +939,20 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
       st.m_c = m_new;
     }
     const float neg_m = (st.m_c == -INFINITY) ? 0.f : -st.m_c;
-    float ls0 = 0.f, ls1 = 0.f;
+    // the fp32 probabilities stay in s: the next MFMA phase adds their row
+    // sums between its PV MFMAs
     constexpr int kCopyEvery = G::NKB * 16 / L2;
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         if ((kb * 16 + j) % kCopyEvery == 0) copy((kb * 16 + j) / kCopyEvery);
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][j], a.c, neg_m));
-        s[kb][j] = p;
-        if (j & 1)
-          ls1 += p;
-        else
-          ls0 += p;
+        s[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][j], a.c, neg_m));
       }
 #pragma unroll
     for (int kc = 0; kc < G::NKC; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[kc >> 1][8 * (kc & 1) + e];
-    st.l += ls0 + ls1;
   };
 
   // ---- phase p0 + I of group GR (I, GR compile-time).  The MFMA phase of
