@@ -831,9 +831,18 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   //  V^T operand from a V^T tile: lane (ql, g), step (kc, db) reads logical
   //  chunk 2kc+g (stored keys 16kc + 8g .. +7, in P's k-slot order) of
   //  feature row db*32 + ql.
+  // The V buffers sit above the 64 KB that a ds_read immediate offset can
+  // reach, so each read offset is kept with a bias of kVtBias in a register
+  // the compiler cannot see through; the buffer's address minus the bias plus
+  // the feature block's offset then fits the immediate field, and no VALU
+  // address add is needed per read.
+  constexpr int kVtBias = 3 * G::kTileBytes;
   int vt_rd[G::NKC];
 #pragma unroll
-  for (int kc = 0; kc < G::NKC; ++kc) vt_rd[kc] = ql * VROW + (((2 * kc + g) ^ vt_swz(ql)) * 16);
+  for (int kc = 0; kc < G::NKC; ++kc) {
+    vt_rd[kc] = ql * VROW + (((2 * kc + g) ^ vt_swz(ql)) * 16) + kVtBias;
+    asm volatile("" : "+v"(vt_rd[kc]));
+  }
 
   RowState<G::NKB, G::NDB> st;
   st.init();
@@ -847,7 +856,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
       constexpr int NSTEP = G::NKC * G::NDB;
       auto read_v = [&](int step) {
         if constexpr (kVt) {
-          return *(const bf16x8*)(vl + (step % G::NDB) * 32 * VROW + vt_rd[step / G::NDB]);
+          return *(const bf16x8*)(vl + ((step % G::NDB) * 32 * VROW - kVtBias) + vt_rd[step / G::NDB]);
         } else {
           const char* p = vl + (step / G::NDB) * 16 * G::ROW + v_rd[step % G::NDB];
           const i16x4 lo4 = lds_read_tr(p);
