@@ -848,6 +848,27 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   st.init();
   f32x16 s[G::NKB];
   bf16x8 pf[G::NKC];
+  // Row sums of P on the matrix cores: a 16x16x32 MFMA reads the P^T operand
+  // registers of the 32x32x16 PV step as its B operand (lane l: keys of its
+  // lane group l/16, query n = l%16 of lanes l%32 < 16, n + 16 of the others)
+  // and an A operand whose row 0 sums lane groups 0 and 2 and row 1 groups 1
+  // and 3, so result rows 0 and 1 (lanes 0..15, registers 0 and 1) are the
+  // 16-key sums of queries n and n + 16.  lsum holds the sums since the last
+  // rescale; st.l takes them over at every rescale and at the end.
+  f32x4 lsum = {};
+  bf16x8 ones_sel;
+  {
+    const __bf16 one = (lane & 15) == ((lane >> 4) & 1) ? (__bf16)1.0f : (__bf16)0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones_sel[e] = one;
+  }
+  // this lane's query's share of lsum (the whole row sum on lane half 0)
+  auto lsum_row = [&]() {
+    const int src = (ql & 15) * 4;
+    const float a0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(lsum[0])));
+    const float a1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(lsum[1])));
+    return g == 0 ? (ql < 16 ? a0 : a1) : 0.f;
+  };
 
   // ---- MFMA phase of tile k: PV of tile k-1 (V in vl), then S of tile k (K in kl).
   auto m_phase = [&](int k, const char* kl, const char* vl) {
@@ -864,11 +885,6 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       };
-      // P(k-1) is still in s as fp32: add its row sums a few per MFMA, where
-      // this wave's VALU slots are otherwise idle (S(k) overwrites s only after).
-      constexpr int kSumPerStep = G::NKB * 16 / NSTEP;
-      static_assert(kSumPerStep * NSTEP == G::NKB * 16, "whole scores per PV step");
-      float ls0 = 0.f, ls1 = 0.f;
       bf16x8 va[VPF + 1];
 #pragma unroll
       for (int step = 0; step < VPF; ++step) va[step] = read_v(step);
@@ -878,20 +894,10 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
         VL_SCHED_BARRIER(0);
         st.o[step % G::NDB] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[step / G::NDB], st.o[step % G::NDB], 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < kSumPerStep; ++t) {
-          const int idx = step * kSumPerStep + t;
-          if (t & 1)
-            ls1 += s[idx >> 4][idx & 15];
-          else
-            ls0 += s[idx >> 4][idx & 15];
-        }
-        // an opaque use keeps the adds in this step (they would otherwise
-        // sink to the sums' only use after the loop)
-        asm volatile("" : "+v"(ls0), "+v"(ls1));
+        if (step % G::NDB == 0)
+          lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_sel, pf[step / G::NDB], lsum, 0, 0, 0);
         VL_SCHED_BARRIER(0);
       }
-      st.l += ls0 + ls1;
     }
     if (k < ntiles) {
       constexpr int KPF = 3;
@@ -940,16 +946,19 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
     const bool need = mx_c > st.m_c + 8.0f;
     if (__ballot(need)) {
       asm volatile("");
-      const float m_new = need ? mx_c : st.m_c;
+      // an integer offset: a weight under any other offset (a later rescale,
+      // another key range of the same row) is the same value times a power of
+      // two (up to the fp32 rounding of s*c - m), so its bf16 rounding does
+      // not depend on where the offset was set; alpha is a power of two
+      const float m_new = need ? ceilf(mx_c) : st.m_c;
       const float alpha = need ? __builtin_amdgcn_exp2f(st.m_c - m_new) : 1.0f;
-      st.l *= alpha;
+      st.l = (st.l + lsum_row()) * alpha;
+      lsum = f32x4{};
 #pragma unroll
       for (int d = 0; d < G::NDB; ++d) st.o[d] *= alpha;
       st.m_c = m_new;
     }
     const float neg_m = (st.m_c == -INFINITY) ? 0.f : -st.m_c;
-    // the fp32 probabilities stay in s: the next MFMA phase adds their row
-    // sums between its PV MFMAs
     constexpr int kCopyEvery = G::NKB * 16 / L2;
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
@@ -1042,7 +1051,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   if (!wave_active) return;
-  const float l_tot = pair_sum(st.l);
+  const float l_tot = pair_sum(st.l + lsum_row());
   if (tr.unit >= 0) {
     float* wo = a.ws + (int64_t)tr.unit * BM * D;
     float2* wml = (float2*)(a.ws + (int64_t)a.slots * BM * D) + (int64_t)tr.unit * BM;

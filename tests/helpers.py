@@ -7,9 +7,17 @@ import torch
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
 F32_MAX_ABS = 1e-5
-# lse is accumulated in fp32 from exact bf16/fp32 products; the bound below is
-# ~100x the expected rounding error of an fp32 log-sum-exp over <= 33k terms.
-LSE_ATOL_BF16 = 1e-3
+# lse of the bf16 varlen kernel is the log of the row sum of the softmax
+# weights after their rounding to bf16 (the same weights that multiply V, so
+# the output's weights sum to one).  Round-to-nearest to bf16's 8-bit
+# significand changes each weight by a relative 2^-8 at most, so the row sum,
+# and with it exp(lse), by the same: |d lse| <= ln(1 + 2^-8) = 3.9e-3, plus
+# fp32 accumulation error far below that.  The roundings are unbiased: over
+# rows that hold a single weight (the worst case, no averaging) the mean of
+# |d lse| is 1.41e-3 for weights spread over an octave, so a systematic
+# offset of 2e-3 fails the mean bound.  The fp32 path sums unrounded weights.
+LSE_ATOL_BF16 = 4e-3
+LSE_MEAN_BF16 = 2e-3
 LSE_ATOL_F32 = 1e-5
 
 
@@ -33,7 +41,10 @@ def check_lse(got: np.ndarray, ref: np.ndarray, f32: bool, what: str):
     d = np.abs(got[~both_inf] - ref[~both_inf])
     tol = LSE_ATOL_F32 if f32 else LSE_ATOL_BF16
     if d.size:
+        print(f"[lse] {what}: max-abs {d.max():.3g} mean-abs {d.mean():.3g}", flush=True)
         assert d.max() <= tol, f"{what}: lse max-abs {d.max():.3g} > {tol}"
+        if not f32:
+            assert d.mean() <= LSE_MEAN_BF16, f"{what}: lse mean-abs {d.mean():.3g} > {LSE_MEAN_BF16}"
 
 
 def sample_rows(cu, block_m: int = 128, n_random: int = 256, seed: int = 0, edge: int = 64):
