@@ -862,6 +862,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones_sel[e] = one;
   }
+  // the lazy rescale threshold (offset + 8) and the negated offset (0 while
+  // no score has been seen), both changed only by a rescale
+  float m_thr = -INFINITY, neg_m = 0.f;
   // this lane's query's share of lsum (the whole row sum on lane half 0)
   auto lsum_row = [&]() {
     const int src = (ql & 15) * 4;
@@ -943,7 +946,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
     mx = pair_max(mx);
     const float mx_c = mx * a.c;
-    const bool need = mx_c > st.m_c + 8.0f;
+    const bool need = mx_c > m_thr;
     if (__ballot(need)) {
       asm volatile("");
       // an integer offset: a weight under any other offset (a later rescale,
@@ -957,8 +960,9 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
 #pragma unroll
       for (int d = 0; d < G::NDB; ++d) st.o[d] *= alpha;
       st.m_c = m_new;
+      m_thr = m_new + 8.0f;
+      neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
     }
-    const float neg_m = (st.m_c == -INFINITY) ? 0.f : -st.m_c;
     constexpr int kCopyEvery = G::NKB * 16 / L2;
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)

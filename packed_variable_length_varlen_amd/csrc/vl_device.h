@@ -42,9 +42,14 @@ __device__ __forceinline__ float swap_halves(float x) {
 }
 
 // x[lane] combined with x[lane xor 32]; symmetric in the two halves.
+// (The max is one v_max_f32: fmaxf would first requiet each permuted value
+// with a max of the value with itself, two more VALU ops; the inputs here are
+// scores, never signalling NaNs.)
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
 }
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
