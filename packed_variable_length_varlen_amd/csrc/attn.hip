@@ -30,6 +30,7 @@
 //  * varlen masks keys only in a request's last, partial tile; block-local
 //    masks each row to [lo, hi) computed from integers (no dense mask, no
 //    device-to-host decision) and loads only the union of the rows' windows.
+#include <cmath>
 #include <mutex>
 #include <type_traits>
 
@@ -1480,7 +1481,9 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   if (num_reqs == 0 || max_q == 0) return VL_OK;
   if (!q || !k || !v || !q_cu || !kv_cu || !out) return VL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
-  if (!(scale == scale)) return VL_EINVAL;
+  // the online softmax tracks the maximum of the raw scores: that is the
+  // maximum of scale * q.k only for scale >= 0
+  if (!(scale >= 0.f) || std::isinf(scale)) return VL_EINVAL;
   const VarlenPlan plan = varlen_plan(kF32, split, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
@@ -1556,7 +1559,9 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
   if (B == 0 || n == 0) return VL_OK;
   if (!q || !k || !v || !out) return VL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
-  if (!(scale == scale)) return VL_EINVAL;
+  // the online softmax tracks the maximum of the raw scores: that is the
+  // maximum of scale * q.k only for scale >= 0
+  if (!(scale >= 0.f) || std::isinf(scale)) return VL_EINVAL;
   if ((int64_t)B * n > INT32_MAX) return VL_EUNSUPPORTED;
   const int nqt = (n + 127) / 128;
   const int64_t G = (int64_t)B * H * nqt;
