@@ -1394,7 +1394,7 @@ __global__ void __launch_bounds__(64) tile_map_kernel(const int32_t* q_cu, const
 
 namespace {
 
-constexpr int kChunk = 16;  // logical tiles kept together on one chiplet
+constexpr int kChunk = 32;  // logical tiles kept together on one chiplet
 // bf16 varlen: the ping-pong kernel, 8 waves, 256 query rows per work-group,
 // 64-key tiles
 constexpr int kBf16VarlenThreads = 512;
