@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(kCopyThreads) copy_segments_kernel(
 #pragma unroll
   for (int i = 0; i < kCopyUnroll; ++i) {
     const int64_t u = u0 + i * kCopyThreads + threadIdx.x;
-    buf[i] = u < real_units ? s[u] : U{};
+    buf[i] = u < real_units ? (kPack ? __builtin_nontemporal_load(s + u) : s[u]) : U{};
   }
   // Streaming stores: the destination is not re-read by this kernel.
 #pragma unroll
@@ -93,7 +93,10 @@ __global__ void __launch_bounds__(kCopyThreads) copy_batch_kernel(CopyBatch cb) 
 #pragma unroll
   for (int k = 0; k < kCopyUnroll; ++k) {
     const int64_t u = u0 + k * kCopyThreads + threadIdx.x;
-    buf[k] = u < real_units ? s[u] : u32x4{};
+    // pack sources (the padded slabs) are streamed once: non-temporal loads
+    // (+2.5-3.5 points of HBM); an unpack source is the attention output just
+    // written, often still in the last-level cache, which they would pass by
+    buf[k] = u < real_units ? (kPack ? __builtin_nontemporal_load(s + u) : s[u]) : u32x4{};
   }
 #pragma unroll
   for (int k = 0; k < kCopyUnroll; ++k) {
