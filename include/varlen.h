@@ -145,9 +145,9 @@ int unpack_cfg_combine(const void* src_flat, const int32_t* seg_cu, const int32_
  *   q, k, v, out: bf16, 16-byte aligned; q_cu/kv_cu: int32 [num_reqs+1] with
  *   cu[0] = 0, non-decreasing (trusted).  max_q / max_kv: upper bounds of the
  *   per-request lengths, used only to size the launch.  D in {64, 128};
- *   H >= 1; num_reqs >= 0; scale finite and >= 0 (else VL_EINVAL: the online
+ *   H >= 1; num_reqs >= 0; scale finite and > 0 (else VL_EINVAL: the online
  *   softmax follows the maximum of the raw scores q.k, which is that of
- *   scale * q.k only for scale >= 0).  The softmax weights are rounded to
+ *   scale * q.k only for scale > 0).  The softmax weights are rounded to
  *   bf16 before the product with V, and the row sum behind the normalisation
  *   and lse is the sum of those rounded weights (so the output's weights sum
  *   to one; lse differs from the exact value by at most ln(1 + 2^-8)).
@@ -205,7 +205,7 @@ int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, i
  *   [b - look_back, b + look_ahead]; no dense n x n mask is formed and only
  *   the keys of that window are read.  q, k, v, out: bf16 [B, n, H, D];
  *   lse: fp32 [B, n, H] or NULL.  D in {64, 128}; B, n >= 0; H >= 1;
- *   block >= 1; look_back, look_ahead >= 0; scale finite and >= 0.
+ *   block >= 1; look_back, look_ahead >= 0; scale finite and > 0.
  * block_local_attn_fwd_f32: same contract on float32 tensors.
  */
 int block_local_attn_fwd(const void* q, const void* k, const void* v, int32_t B, int32_t n,

@@ -127,7 +127,8 @@ __device__ __forceinline__ TileRange tile_range(const AttnArgs& a) {
     t.seq_q0 = i0;
     const int nb = (a.n + a.block - 1) / a.block;
     const int blo = max(0, i0 / a.block - a.look_back);
-    const int bhi = min(nb - 1, (i1 - 1) / a.block + a.look_ahead);
+    const int blast = (i1 - 1) / a.block;
+    const int bhi = blast + min(a.look_ahead, nb - 1 - blast);  // (no overflow for any look_ahead)
     t.k_lo = blo * a.block;
     t.k_hi = min(a.n, (bhi + 1) * a.block);
   }
@@ -139,7 +140,7 @@ __device__ __forceinline__ void window_of(const AttnArgs& a, int i, int& lo, int
   const int nb = (a.n + a.block - 1) / a.block;
   const int b = i / a.block;
   lo = max(0, b - a.look_back) * a.block;
-  hi = min(a.n, (min(nb - 1, b + a.look_ahead) + 1) * a.block);
+  hi = min(a.n, (b + min(a.look_ahead, nb - 1 - b) + 1) * a.block);
 }
 
 // ---------------------------------------------------------------- online softmax
@@ -1255,6 +1256,114 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- block-local fp32, block-aligned
+
+// Block-local attention in fp32 with the work cut along the blocks: every
+// query of block b sees the same keys (the frames of blocks
+// [b - look_back, b + look_ahead] that exist), so one wave takes one query
+// block of one (batch, head) -- up to 32 rows, the MFMA tile's width -- and
+// only its window's keys, in chunks of 32.  No LDS and no barrier: K is read
+// straight into the A operand registers, V element by element (the lanes of
+// a half read one 128-byte row segment).  Against tiles of 128 rows over the
+// union of their rows' windows this cuts the fp32 MFMA work 2-4.5x at the
+// Token2Wav shape (24-frame blocks).
+//   S^T = K Q^T with v_mfma_f32_32x32x2_f32: lane (ql, g) holds features
+//   [32g, 32g + 32) of query row ql (B operand) and of key row ql of the
+//   chunk (A operand); step s contracts feature 32g + s of both halves.  The
+//   result gives lane (ql, g) the scores of query ql for keys score_key(0, j, g).
+//   O^T += V^T P^T: step j contracts key score_key(0, j, g) of each half, whose
+//   probability is the lane's own score register j (see the tiled kernel).
+template <int D>
+__global__ void __launch_bounds__(256) block_local_f32_kernel(AttnArgs a) {
+  static_assert(D == 64, "two lane halves of 32 features");
+  constexpr int NQ = D / 2;
+  constexpr int NDB = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int ql = lane & 31;
+  const int g = lane >> 5;
+  const int nb = (a.n + a.block - 1) / a.block;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= (int64_t)a.B * a.H * nb) return;
+  const int qb = (int)(unit % nb);  // neighbouring blocks (shared keys) in neighbouring waves
+  const int h = (int)((unit / nb) % a.H);
+  const int b = (int)(unit / ((int64_t)nb * a.H));
+  const int H = a.H;
+  const int64_t row_stride = (int64_t)H * D;
+  const int64_t base = (int64_t)b * a.n * row_stride + (int64_t)h * D;
+
+  const int r0 = qb * a.block;
+  const int nq = min(a.block, a.n - r0);
+  const int k_lo = max(0, qb - a.look_back) * a.block;
+  const int k_hi = min((qb + min(a.look_ahead, nb - 1 - qb)) * a.block + a.block, a.n);
+
+  const float* __restrict__ qg = (const float*)a.q;
+  const float* __restrict__ kg = (const float*)a.k;
+  const float* __restrict__ vg = (const float*)a.v;
+
+  // query rows past the block's end repeat its last row (computed, not stored)
+  float qf[NQ];
+  {
+    const float* qp = qg + base + (int64_t)(r0 + min(ql, nq - 1)) * row_stride + g * NQ;
+#pragma unroll
+    for (int s4 = 0; s4 < NQ / 4; ++s4) {
+      const f32x4 x = *(const f32x4*)(qp + 4 * s4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * s4 + e] = x[e];
+    }
+  }
+
+  RowState<1, NDB> st;
+  st.init();
+  for (int key0 = k_lo; key0 < k_hi; key0 += 32) {
+    // keys past the window's end read its last row (finite; masked below)
+    float kf[NQ];
+    {
+      const float* kp = kg + base + (int64_t)min(key0 + ql, k_hi - 1) * row_stride + g * NQ;
+#pragma unroll
+      for (int s4 = 0; s4 < NQ / 4; ++s4) {
+        const f32x4 x = *(const f32x4*)(kp + 4 * s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kf[4 * s4 + e] = x[e];
+      }
+    }
+    float vf[16][NDB];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float* vp = vg + base + (int64_t)min(key0 + score_key(0, j, g), k_hi - 1) * row_stride + ql;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vf[j][db] = vp[db * 32];
+    }
+    f32x16 s[1] = {f32x16{}};
+#pragma unroll
+    for (int st4 = 0; st4 < NQ; ++st4) s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[st4], qf[st4], s[0], 0, 0, 0);
+    if (key0 + 32 > k_hi) mask_scores<1>(s, key0, g, k_lo, k_hi);
+    st.softmax_tile(s, a.c);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[j][db], s[0][j], st.o[db], 0, 0, 0);
+  }
+
+  const float l_tot = pair_sum(st.l);
+  if (ql < nq) {
+    const int64_t row = base + (int64_t)(r0 + ql) * row_stride;
+    float* op = (float*)a.out + row;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + 8 * i + 4 * g;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = l_tot > 0.f ? st.o[db][4 * i + e] / l_tot : 0.f;
+        *(f32x4*)(op + d) = w;
+      }
+    if (a.lse != nullptr && g == 0)
+      a.lse[((int64_t)b * a.n + r0 + ql) * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- split merge
 
 // Merges the partial results of the split work items.  Tail tile t's key
@@ -1482,8 +1591,9 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   if (!q || !k || !v || !q_cu || !kv_cu || !out) return VL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
   // the online softmax tracks the maximum of the raw scores: that is the
-  // maximum of scale * q.k only for scale >= 0
-  if (!(scale >= 0.f) || std::isinf(scale)) return VL_EINVAL;
+  // maximum of scale * q.k only for scale > 0 (and a masked score, -inf,
+  // times a zero scale would be NaN)
+  if (!(scale > 0.f) || std::isinf(scale)) return VL_EINVAL;
   const VarlenPlan plan = varlen_plan(kF32, split, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
@@ -1560,8 +1670,9 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
   if (!q || !k || !v || !out) return VL_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
   // the online softmax tracks the maximum of the raw scores: that is the
-  // maximum of scale * q.k only for scale >= 0
-  if (!(scale >= 0.f) || std::isinf(scale)) return VL_EINVAL;
+  // maximum of scale * q.k only for scale > 0 (and a masked score, -inf,
+  // times a zero scale would be NaN)
+  if (!(scale > 0.f) || std::isinf(scale)) return VL_EINVAL;
   if ((int64_t)B * n > INT32_MAX) return VL_EUNSUPPORTED;
   const int nqt = (n + 127) / 128;
   const int64_t G = (int64_t)B * H * nqt;
@@ -1577,11 +1688,18 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
   a.B = B;
   a.n = n;
   a.block = block;
-  a.look_back = look_back;
-  a.look_ahead = look_ahead;
+  // windows wider than the sequence are the whole sequence
+  const int nblocks = (n + block - 1) / block;
+  a.look_back = min(look_back, nblocks);
+  a.look_ahead = min(look_ahead, nblocks);
   a.nqt = nqt;
   (void)hipGetLastError();
-  if (kF32) {
+  if (kF32 && D == 64 && block <= 32) {
+    // one wave per query block of one (batch, head)
+    const int64_t units = (int64_t)B * H * ((n + block - 1) / block);
+    if ((units + 3) / 4 > INT32_MAX) return VL_EUNSUPPORTED;
+    hipLaunchKernelGGL((vl::block_local_f32_kernel<64>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+  } else if (kF32) {
     if (D == 128)
       hipLaunchKernelGGL((vl::attn_f32_kernel<128, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
     else

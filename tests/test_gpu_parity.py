@@ -564,17 +564,29 @@ def test_block_local_vs_oracle(n, win, f32):
     check_lse(to64(lse), rl, f32, f"block-local n={n} {win}")
 
 
+# (the fp32 entry takes one wave per query block when D = 64 and block <= 32:
+# blocks of 1, 17, 24 and 32 frames, a sequence shorter than one block, and
+# windows wider than the sequence -- up to the largest int -- on both paths)
 @pytest.mark.parametrize("case", [(2, 300, 7, 2, 1, 128), (1, 33, 40, 0, 0, 64), (3, 61, 5, 3, 0, 128),
-                                  (1, 500, 24, 30, 30, 64)])
-def test_block_local_other_shapes(case):
+                                  (1, 500, 24, 30, 30, 64), (2, 301, 17, 2, 3, 64), (1, 5, 24, 0, 0, 64),
+                                  (1, 96, 32, 1, 1, 64), (1, 70, 1, 3, 2, 64),
+                                  (1, 100, 24, 0, 2147483647, 64), (1, 100, 24, 2147483647, 1, 128)])
+@pytest.mark.parametrize("f32", [False, True])
+def test_block_local_other_shapes(case, f32):
     B, n, block, lb, la, D = case
-    log(f"[block_local] B={B} n={n} block={block} lb={lb} la={la} D={D}")
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[block_local] B={B} n={n} block={block} lb={lb} la={la} D={D} {dtype}")
     rng = np.random.default_rng(n)
-    q, k, v = (torch.from_numpy(rng.standard_normal((B, n, 2, D)).astype(np.float32)).to(torch.bfloat16)
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, n, 2, D)).astype(np.float32)).to(dtype)
                for _ in range(3))
-    out = vl.block_local_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), block, lb, la, wl.softmax_scale(D))
-    ro, _ = oracle.block_local_attention(to64(q), to64(k), to64(v), block, lb, la, wl.softmax_scale(D))
-    check_close(to64(out), ro, False, f"block-local {case}")
+    fn = vl.block_local_attn_fwd_f32 if f32 else vl.block_local_attn_fwd
+    full, out = canary_out(tuple(q.shape), dtype, pad=1)
+    _, lse = fn(q.to(DEV), k.to(DEV), v.to(DEV), block, lb, la, wl.softmax_scale(D), out=out, return_lse=True)
+    torch.cuda.synchronize()
+    assert_canary(full, pad=1)
+    ro, rl = oracle.block_local_attention(to64(q), to64(k), to64(v), block, lb, la, wl.softmax_scale(D))
+    check_close(to64(out), ro, f32, f"block-local {case}")
+    check_lse(to64(lse), rl, f32, f"block-local {case}")
 
 
 def test_block_local_own_block_equals_varlen_bitwise_free_check():

@@ -61,8 +61,8 @@ def test_bad_scalars_rejected_before_launch(lib):
     assert lib.varlen_attn_fwd(odd, p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, None) == VL_EINVAL
     # NaN scale
     assert lib.varlen_attn_fwd(p, p, p, p, p, 8, 8, 1, 2, 64, float("nan"), p, None, None) == VL_EINVAL
-    # negative or infinite scale (the running maximum is taken over raw scores)
-    for bad in (-0.125, float("inf"), float("-inf")):
+    # zero, negative or infinite scale (the running maximum is taken over raw scores)
+    for bad in (0.0, -0.125, float("inf"), float("-inf")):
         assert lib.varlen_attn_fwd(p, p, p, p, p, 8, 8, 1, 2, 64, bad, p, None, None) == VL_EINVAL
         assert lib.varlen_attn_fwd_f32(p, p, p, p, p, 8, 8, 1, 2, 64, bad, p, None, None) == VL_EINVAL
         assert lib.block_local_attn_fwd(p, p, p, 1, 10, 2, 64, 24, 0, 0, bad, p, None, None) == VL_EINVAL
