@@ -1364,6 +1364,123 @@ __global__ void __launch_bounds__(256) block_local_f32_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- block-local bf16, block-aligned
+
+// The bf16 counterpart of block_local_f32_kernel (D = 64, blocks of <= 32
+// frames): one wave per query block of one (batch, head), its window's keys
+// in chunks of 32, no LDS, no barriers.  Operands as in the varlen kernel:
+//   S^T = K Q^T (v_mfma_f32_32x32x16_bf16, 4 steps over D): lane (ql, g)
+//   holds features 16 ds + 8g .. +7 of query row ql (B) and of key row ql of
+//   the chunk (A), one 16-byte load each.
+//   O^T += V^T P^T (2 key steps x 2 feature blocks): P^T(kc) is the lane's
+//   score registers 8kc .. 8kc+7 rounded to bf16, i.e. keys
+//   16kc + 4g + (i & 3) + 8(i >> 2), i = 0..7; the V^T operand of lane (ql, g)
+//   holds feature 32 db + ql of those same keys, gathered element by element
+//   (a lane half reads 64 contiguous bytes of one key row per element).
+template <int D>
+__global__ void __launch_bounds__(256) block_local_bf16_kernel(AttnArgs a) {
+  static_assert(D == 64, "four 16-feature MFMA steps");
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int ql = lane & 31;
+  const int g = lane >> 5;
+  const int nb = (a.n + a.block - 1) / a.block;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= (int64_t)a.B * a.H * nb) return;
+  const int qb = (int)(unit % nb);  // neighbouring blocks (shared keys) in neighbouring waves
+  const int h = (int)((unit / nb) % a.H);
+  const int b = (int)(unit / ((int64_t)nb * a.H));
+  const int H = a.H;
+  const int64_t row_stride = (int64_t)H * D;
+  const int64_t base = (int64_t)b * a.n * row_stride + (int64_t)h * D;
+
+  const int r0 = qb * a.block;
+  const int nq = min(a.block, a.n - r0);
+  const int k_lo = max(0, qb - a.look_back) * a.block;
+  const int k_hi = min((qb + min(a.look_ahead, nb - 1 - qb)) * a.block + a.block, a.n);
+
+  const __bf16* __restrict__ qg = (const __bf16*)a.q;
+  const __bf16* __restrict__ kg = (const __bf16*)a.k;
+  const __bf16* __restrict__ vg = (const __bf16*)a.v;
+
+  // query rows past the block's end repeat its last row (computed, not stored)
+  bf16x8 qf[NDS];
+  {
+    const __bf16* qp = qg + base + (int64_t)(r0 + min(ql, nq - 1)) * row_stride + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = *(const bf16x8*)(qp + 16 * ds);
+  }
+
+  RowState<1, NDB> st;
+  st.init();
+  // keys past the window's end read its last row (finite; masked below)
+  auto load_chunk = [&](int key0, bf16x8 (&kf)[NDS], bf16x8 (&vt)[2][NDB]) {
+    const __bf16* kp = kg + base + (int64_t)min(key0 + ql, k_hi - 1) * row_stride + 8 * g;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kf[ds] = *(const bf16x8*)(kp + 16 * ds);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = min(key0 + 16 * kc + 4 * g + (i & 3) + 8 * (i >> 2), k_hi - 1);
+        const __bf16* vp = vg + base + (int64_t)key * row_stride + ql;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vt[kc][db][i] = vp[32 * db];
+      }
+  };
+  auto compute_chunk = [&](int key0, const bf16x8 (&kf)[NDS], const bf16x8 (&vt)[2][NDB]) {
+    f32x16 s[1] = {f32x16{}};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[ds], s[0], 0, 0, 0);
+    if (key0 + 32 > k_hi) mask_scores<1>(s, key0, g, k_lo, k_hi);
+    st.softmax_tile(s, a.c);
+    bf16x8 pf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[0][8 * kc + e];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[kc][db], pf[kc], st.o[db], 0, 0, 0);
+  };
+  // chunk c + 1 is loaded while chunk c is computed (two register sets)
+  bf16x8 kfa[NDS], vta[2][NDB], kfb[NDS], vtb[2][NDB];
+  load_chunk(k_lo, kfa, vta);  // the window is never empty
+  for (int key0 = k_lo;;) {
+    const int k1 = key0 + 32;
+    if (k1 < k_hi) load_chunk(k1, kfb, vtb);
+    compute_chunk(key0, kfa, vta);
+    if (k1 >= k_hi) break;
+    const int k2 = k1 + 32;
+    if (k2 < k_hi) load_chunk(k2, kfa, vta);
+    compute_chunk(k1, kfb, vtb);
+    if (k2 >= k_hi) break;
+    key0 = k2;
+  }
+
+  const float l_tot = pair_sum(st.l);
+  if (ql < nq) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    __bf16* op = (__bf16*)a.out + base + (int64_t)(r0 + ql) * row_stride;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + 8 * i + 4 * g;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[db][4 * i + e] * inv);
+        *(bf16x4*)(op + d) = w;
+      }
+    if (a.lse != nullptr && g == 0)
+      a.lse[((int64_t)b * a.n + r0 + ql) * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------- split merge
 
 // Merges the partial results of the split work items.  Tail tile t's key
@@ -1704,6 +1821,13 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
       hipLaunchKernelGGL((vl::attn_f32_kernel<128, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
+  } else if (D == 64 && block <= 32 && (int64_t)(1 + a.look_back + a.look_ahead) * block <= 64) {
+    // windows of up to two 32-key chunks (own block, one neighbour at blocks
+    // of 24): one wave per query block; wider windows go to the tiled kernel,
+    // whose pipelined tiles hide their loads better
+    const int64_t units = (int64_t)B * H * ((n + block - 1) / block);
+    if ((units + 3) / 4 > INT32_MAX) return VL_EUNSUPPORTED;
+    hipLaunchKernelGGL((vl::block_local_bf16_kernel<64>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL((vl::attn_bf16_kernel<128, 4, 1, 64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
