@@ -882,7 +882,7 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
       constexpr int NSTEP = G::NKC * G::NDB;
       auto read_v = [&](int step) {
         if constexpr (kVt) {
-          return *(const bf16x8*)(vl + ((step % G::NDB) * 32 * VROW - kVtBias) + vt_rd[step / G::NDB]);
+          return *(const bf16x8*)(vl + (((step % G::NDB) * 32 * VROW - kVtBias) + vt_rd[step / G::NDB]));
         } else {
           const char* p = vl + (step / G::NDB) * 16 * G::ROW + v_rd[step % G::NDB];
           const i16x4 lo4 = lds_read_tr(p);
