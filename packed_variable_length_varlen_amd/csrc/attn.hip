@@ -214,7 +214,7 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[NKB], int key0, int g, i
 // s_waitcnt immediate (gfx9 encoding) that waits for all vector-memory operations.
 constexpr int kWaitVm0 = 0x0F70;
 // Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
+[[maybe_unused]] constexpr int kBufferFlags = 0x00020000;  // (used in the device pass only)
 
 template <int D, int WAVES, int BN_>
 struct Bf16Geo {
