@@ -345,6 +345,43 @@ def test_varlen_loose_max_bounds_and_large_values():
     check_close(to64(o3), ro, False, "scaled q")
 
 
+@pytest.mark.parametrize("f32", [False, True])
+def test_varlen_growing_scores_rescale(f32):
+    """Key norms ramp from 1x to 60x along each request, so the row maxima
+    climb by far more than 2^8 (in exp2 units, up to ~400) many times over
+    the key tiles: every lazy rescale (and, on the bf16 path, the fold of the
+    matrix-core row sums into the running sum at a rescale) is exercised,
+    and the weights of a fixed offset would overflow.  Unsplit and split
+    launches against the oracle."""
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[varlen] growing scores {dtype}")
+    ql = [700, 1500, 129]
+    H, D = 2, 128
+    q, k, v = wl.random_varlen_case(43, ql, H, D, torch.float32)
+    cu = oracle.cu_seqlens_from_lengths(ql)
+    ramp = torch.cat([torch.linspace(1.0, 60.0, n) for n in ql]).reshape(-1, 1, 1)
+    q, k, v = q.to(dtype), (k * ramp).to(dtype), v.to(dtype)
+    scale = wl.softmax_scale(D)
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), cu, cu, scale)
+    assert rl.max() > 200.0, "the case must drive the scores far past one rescale step"
+    for split in ([False] if f32 else [False, True]):
+        out, lse = _run_varlen(q, k, v, cu, cu, scale, f32, split=split)
+        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+        if f32:
+            # the fp32 bound (1e-5) holds for unit-scale inputs; the fp32
+            # rounding of a dot product grows with its magnitude, here up to
+            # 60x (lse ~ 280 alone has an fp32 ulp of 3e-5), so the bound
+            # scales by the ramp's top factor
+            tol = 60 * 1e-5
+            eo = np.abs(to64(out) - ro).max()
+            el = np.abs(to64(lse) - rl).max()
+            log(f"   fp32 out max-abs {eo:.3g}, lse max-abs {el:.3g} (bound {tol:.3g})")
+            assert eo <= tol and el <= tol
+        else:
+            check_close(to64(out), ro, f32, f"growing scores split={split}")
+            check_lse(to64(lse), rl, f32, f"growing scores split={split}")
+
+
 def test_varlen_invariants_bitwise():
     """Alone == inside the packed batch, permutation permutes outputs, and two
     runs give the same bits (the tiles never mix requests)."""
