@@ -330,6 +330,46 @@ def main():
     err(f"[bench] block-local production (flushed) us: "
         f"{[(d['dtype'], d['look_back'], d['look_ahead'], d['us_median']) for d in detail['block_local_production']]}")
 
+    # The attention call alone at the other full-size workloads (same launch,
+    # per-call HIP events, median of 10): their token layout from the recipe's
+    # text-length draws, Q/K/V N(0,1) drawn on the device (seeded).
+    detail["attention_other_workloads"] = []
+    for other in ("joint-16k", "mixres-4req", "edit-cfg-4seq"):
+        if other == args.workload:
+            continue
+        ospec = wl.WORKLOADS[other]
+        lens = wl.varlen_lengths(ospec)
+        oT = sum(lens)
+        ocu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(ospec.seed)
+        oq, ok_, ov = (torch.randn((oT, ospec.H, ospec.D), generator=gen, device=dev).to(torch.bfloat16)
+                       for _ in range(3))
+        oout = torch.empty_like(oq)
+        ows = torch.empty(vl.varlen_split_workspace_bytes(oT, len(lens), ospec.H, ospec.D), dtype=torch.uint8,
+                          device=dev)
+        ofn = lambda: vl.varlen_attn_fwd_split(oq, ok_, ov, ocu, ocu, max(lens), max(lens), wl.softmax_scale(ospec.D),
+                                               out=oout, workspace=ows)
+        for _ in range(3):
+            ofn()
+        oev = []
+        for _ in range(10):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            ofn()
+            b.record(stream)
+            oev.append((a, b))
+        torch.cuda.synchronize()
+        oms = float(np.median([a.elapsed_time(b) for a, b in oev]))
+        oflop = 4.0 * ospec.D * ospec.H * sum(x * x for x in lens)
+        otf = oflop / (oms * 1e-3) / 1e12
+        detail["attention_other_workloads"].append({
+            "workload": ospec.name, "total_tokens": oT, "requests": len(lens), "ms_median": round(oms, 4),
+            "TFLOP/s": round(otf, 2), "pct_of_bf16_peak": round(100 * otf / BF16_PEAK_TFLOPS, 2)})
+        err(f"[bench] attention at {other}: {oms:.3f} ms = {otf:.1f} TFLOP/s ({100 * otf / BF16_PEAK_TFLOPS:.1f}%)")
+        del oq, ok_, ov, oout, ows
+
     cpu = None
     if not args.no_cpu_baseline:
         err("[bench] timing the CPU oracle on a bounded sample")

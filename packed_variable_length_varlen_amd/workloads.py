@@ -141,6 +141,15 @@ def make_varlen_inputs(spec: VarlenSpec, dtype: torch.dtype = torch.bfloat16,
                         slabs["q"][1], slabs["k"][1], slabs["v"][1], softmax_scale(D))
 
 
+def varlen_lengths(spec: VarlenSpec, seed: Optional[int] = None) -> List[int]:
+    """Per-request joint lengths (text + image tokens) of a workload: the text
+    lengths are the same first draws of the same generator as in
+    make_varlen_inputs, without drawing the tensors."""
+    rng = np.random.default_rng(spec.seed if seed is None else seed)
+    text_len = [int(rng.integers(lo, hi + 1)) for lo, hi in spec.text_ranges]
+    return [t + int(h) * int(w) for t, (h, w) in zip(text_len, spec.img_grids)]
+
+
 def random_varlen_case(seed: int, lengths: List[int], H: int, D: int, dtype: torch.dtype,
                        kv_lengths: Optional[List[int]] = None):
     """Packed q [sum(lengths), H, D] and k/v [sum(kv_lengths), H, D] N(0,1) draws

@@ -152,3 +152,21 @@ def test_mixfusion_plan_native_matches_oracle_and_pages(lib):
         assert vl.mixfusion_chunk_plan(counts) == oracle.mixfusion_chunk_plan(counts)
     with pytest.raises(vl.VarlenError):
         vl.mixfusion_chunk_plan([5, 0])
+
+
+def test_workload_lengths_match_the_generated_inputs():
+    """varlen_lengths (used by bench.py to lay out the other workloads) takes
+    the same text-length draws as make_varlen_inputs."""
+    import torch
+    from packed_variable_length_varlen_amd import workloads as wl
+    for name in ("tiny-3req",):
+        spec = wl.WORKLOADS[name]
+        inp = wl.make_varlen_inputs(spec, torch.float32)
+        assert wl.varlen_lengths(spec) == [t + i for t, i in zip(inp.text_len, inp.img_tokens)]
+    # the full-size layouts: text drawn in the configured ranges, image grids as configured
+    for name in ("joint-16k", "mixres-4req", "edit-cfg-4seq"):
+        spec = wl.WORKLOADS[name]
+        lens = wl.varlen_lengths(spec)
+        assert len(lens) == len(spec.img_grids)
+        for n, (lo, hi), (h, w) in zip(lens, spec.text_ranges, spec.img_grids):
+            assert lo <= n - h * w <= hi
