@@ -170,3 +170,23 @@ def test_workload_lengths_match_the_generated_inputs():
         assert len(lens) == len(spec.img_grids)
         for n, (lo, hi), (h, w) in zip(lens, spec.text_ranges, spec.img_grids):
             assert lo <= n - h * w <= hi
+
+
+def test_bench_pair_counts_match_the_oracle():
+    """The FLOP counts bench.py reports (4 D H per in-request or in-window
+    pair) rest on its pair counts: block-local pairs equal the oracle's key
+    ranges summed over frames and the True entries of the dense
+    block-difference mask; the vocoder shape gives the counts 47,929 / 95,425
+    / 142,921 (own block / one neighbour / both); varlen pairs equal the
+    entries of the block-diagonal mask."""
+    import numpy as np
+    import bench
+    for n, block in ((10, 24), (96, 24), (101, 24), (2003, 24), (70, 1), (33, 40)):
+        for lb, la in ((0, 0), (1, 0), (0, 1), (1, 1), (3, 2)):
+            by_range = sum(hi - lo for lo, hi in (oracle.block_local_key_range(i, n, block, lb, la) for i in range(n)))
+            dense = int(np.count_nonzero(oracle.block_difference_mask(n, block, lb, la)))
+            assert bench.block_local_pairs(n, block, lb, la) == by_range == dense, (n, block, lb, la)
+    assert [bench.block_local_pairs(2003, 24, lb, la) for lb, la in ((0, 0), (1, 0), (0, 1), (1, 1))] == \
+        [47929, 95425, 95425, 142921]
+    cu = oracle.cu_seqlens_from_lengths([17, 0, 64, 129, 1])
+    assert bench.varlen_pairs(cu) == int(np.count_nonzero(oracle.block_diagonal_mask(cu, cu)))
