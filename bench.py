@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="joint-16k", choices=["joint-16k", "mixres-4req", "edit-cfg-4seq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the attention timings at the other full-size workloads (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -335,7 +337,7 @@ def main():
     # text-length draws, Q/K/V N(0,1) drawn on the device (seeded).
     detail["attention_other_workloads"] = []
     for other in ("joint-16k", "mixres-4req", "edit-cfg-4seq"):
-        if other == args.workload:
+        if other == args.workload or args.no_other_workloads:
             continue
         ospec = wl.WORKLOADS[other]
         lens = wl.varlen_lengths(ospec)
