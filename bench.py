@@ -370,6 +370,40 @@ def main():
             "workload": ospec.name, "total_tokens": oT, "requests": len(lens), "ms_median": round(oms, 4),
             "TFLOP/s": round(otf, 2), "pct_of_bf16_peak": round(100 * otf / BF16_PEAK_TFLOPS, 2)})
         err(f"[bench] attention at {other}: {oms:.3f} ms = {otf:.1f} TFLOP/s ({100 * otf / BF16_PEAK_TFLOPS:.1f}%)")
+        if other == "edit-cfg-4seq":
+            # the per-request CFG combine fused into the unpack of this output:
+            # sequences [r1+, r1-, r2+, r2-], image rows after each text piece,
+            # true CFG scale 4.0; reads two rows and writes one per output row
+            img = [int(h) * int(w) for h, w in ospec.img_grids]
+            ocu_h = np.concatenate([[0], np.cumsum(lens)])
+            nreq = len(lens) // 2
+            pos = torch.tensor([ocu_h[2 * r] + lens[2 * r] - img[2 * r] for r in range(nreq)], dtype=torch.int32,
+                               device=dev)
+            neg = torch.tensor([ocu_h[2 * r + 1] + lens[2 * r + 1] - img[2 * r + 1] for r in range(nreq)],
+                               dtype=torch.int32, device=dev)
+            seg = torch.tensor(np.concatenate([[0], np.cumsum(img[0::2])]), dtype=torch.int32, device=dev)
+            cfg_s = torch.full((nreq,), 4.0, dtype=torch.float32, device=dev)
+            cdst = torch.empty((nreq, max(img[0::2]), ospec.H, ospec.D), dtype=torch.bfloat16, device=dev)
+            cfn = lambda: vl.unpack_cfg_combine(oout, seg, pos, neg, cfg_s, cdst)
+            for _ in range(3):
+                cfn()
+            cev = []
+            for _ in range(10):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                cfn()
+                b.record(stream)
+                cev.append((a, b))
+            torch.cuda.synchronize()
+            cus = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+            cbytes = 3 * sum(img[0::2]) * ospec.H * ospec.D * 2
+            detail["cfg_combine_unpack"] = {"workload": ospec.name, "bytes": int(cbytes), "us_median": round(cus, 2),
+                                            "GB/s": round(cbytes / cus / 1e3, 1),
+                                            "pct_of_hbm": round(100 * cbytes / cus / 1e3 / HBM_PEAK_GBS, 1)}
+            err(f"[bench] CFG combine + unpack at {other}: {cus:.1f} us, "
+                f"{100 * cbytes / cus / 1e3 / HBM_PEAK_GBS:.1f}% of HBM")
+            del cdst
         del oq, ok_, ov, oout, ows
 
     cpu = None
