@@ -21,7 +21,7 @@ __all__ = [
     "unpack_by_cu_seqlens_batched", "varlen_attn_fwd", "varlen_attn_fwd_split",
     "varlen_split_workspace_bytes", "varlen_attn_fwd_f32",
     "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
-    "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError",
+    "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError", "validate_cu_seqlens",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -284,8 +284,26 @@ def _attn_prep(q, k, v, dtype):
         raise VarlenError("q, k, v must agree on heads and head_dim, and k, v on shape")
 
 
+def validate_cu_seqlens(cu, rows: int, max_len: int, what: str = "cu_seqlens") -> None:
+    """Host-side check of a cu_seqlens array the kernels take on trust:
+    cu[0] = 0, non-decreasing, cu[-1] <= rows (the packed tensor's rows), and
+    every length <= max_len (the bound that sized the launch).  Raises
+    VarlenError.  `cu` is a sequence of ints or a tensor (copied to the host,
+    which synchronises with the device)."""
+    c = [int(x) for x in (cu.tolist() if isinstance(cu, torch.Tensor) else cu)]
+    if not c or c[0] != 0:
+        raise VarlenError(f"{what}[0] must be 0")
+    for i in range(len(c) - 1):
+        if c[i + 1] < c[i]:
+            raise VarlenError(f"{what} must be non-decreasing ({what}[{i + 1}] < {what}[{i}])")
+        if c[i + 1] - c[i] > max_len:
+            raise VarlenError(f"request {i} has {c[i + 1] - c[i]} rows, more than the bound {max_len}")
+    if c[-1] > rows:
+        raise VarlenError(f"{what}[-1] = {c[-1]} exceeds the {rows} rows of the packed tensor")
+
+
 def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse, padded_tokens,
-            attn_mask, return_lse, stream, workspace=None):
+            attn_mask, return_lse, stream, workspace=None, check_cu_seqlens=False):
     # The flat path rejects attention masks and needs padded_tokens == 0
     # (vLLM-Omni PR #6711, "Reference / Acknowledgement").
     if attn_mask is not None:
@@ -300,6 +318,9 @@ def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse
     R = q_cu.numel() - 1
     if kv_cu.numel() != R + 1:
         raise VarlenError("q_cu_seqlens and kv_cu_seqlens disagree on the number of requests")
+    if check_cu_seqlens:
+        validate_cu_seqlens(q_cu, q.shape[0], int(max_q), "q_cu_seqlens")
+        validate_cu_seqlens(kv_cu, k.shape[0], int(max_kv), "kv_cu_seqlens")
     T, H, D = q.shape
     if scale is None:
         scale = D ** -0.5
@@ -341,29 +362,35 @@ def varlen_split_workspace_bytes(kv_rows: int, num_reqs: int, H: int, D: int) ->
 
 def varlen_attn_fwd(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
                     lse=None, padded_tokens: int = 0, attn_mask=None, return_lse: bool = False,
-                    stream=None):
-    """bf16 packed [T, H, D] varlen attention; returns out (and lse if asked)."""
+                    stream=None, check_cu_seqlens: bool = False):
+    """bf16 packed [T, H, D] varlen attention; returns out (and lse if asked).
+    check_cu_seqlens: validate both arrays on the host first (a device sync;
+    the kernels take them on trust)."""
     return _varlen("varlen_attn_fwd", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
-                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream)
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream,
+                   check_cu_seqlens=check_cu_seqlens)
 
 
 def varlen_attn_fwd_split(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
                           lse=None, workspace: Optional[torch.Tensor] = None, padded_tokens: int = 0,
-                          attn_mask=None, return_lse: bool = False, stream=None):
+                          attn_mask=None, return_lse: bool = False, stream=None,
+                          check_cu_seqlens: bool = False):
     """varlen_attn_fwd through a workspace: V is staged transposed there, and
     the last partial round is cut along the keys.  `workspace` (a device
     buffer of varlen_split_workspace_bytes(k.shape[0], num_reqs, H, D) bytes)
     is allocated when not given."""
     return _varlen("varlen_attn_fwd_split", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
-                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace)
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace,
+                   check_cu_seqlens=check_cu_seqlens)
 
 
 def varlen_attn_fwd_f32(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
                         lse=None, padded_tokens: int = 0, attn_mask=None, return_lse: bool = False,
-                        stream=None):
+                        stream=None, check_cu_seqlens: bool = False):
     """float32 packed [T, H, D] varlen attention; returns out (and lse if asked)."""
     return _varlen("varlen_attn_fwd_f32", torch.float32, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
-                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream)
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream,
+                   check_cu_seqlens=check_cu_seqlens)
 
 
 def _block_local(fn_name, dtype, q, k, v, block, look_back, look_ahead, scale, out, lse, return_lse,

@@ -382,6 +382,27 @@ def test_varlen_growing_scores_rescale(f32):
             check_lse(to64(lse), rl, f32, f"growing scores split={split}")
 
 
+def test_varlen_check_cu_seqlens_option():
+    """check_cu_seqlens=True validates on the host before the launch: a valid
+    array gives the same bits as the unchecked call, malformed ones raise and
+    never reach the kernels."""
+    log("[varlen] check_cu_seqlens")
+    ql = [17, 64, 129]
+    q, k, v = (t.to(DEV) for t in wl.random_varlen_case(47, ql, 2, 64, torch.bfloat16))
+    cu = torch.tensor([0, 17, 81, 210], dtype=torch.int32, device=DEV)
+    for fn in (vl.varlen_attn_fwd, vl.varlen_attn_fwd_split):
+        o1 = fn(q, k, v, cu, cu, 129, 129)
+        o2 = fn(q, k, v, cu, cu, 129, 129, check_cu_seqlens=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        for bad in ([0, 17, 16, 210], [0, 17, 81, 211], [1, 17, 81, 210]):
+            bcu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+            with pytest.raises(vl.VarlenError):
+                fn(q, k, v, bcu, bcu, 129, 129, check_cu_seqlens=True)
+        with pytest.raises(vl.VarlenError):  # a length past the launch bound
+            fn(q, k, v, cu, cu, 100, 100, check_cu_seqlens=True)
+
+
 def test_varlen_invariants_bitwise():
     """Alone == inside the packed batch, permutation permutes outputs, and two
     runs give the same bits (the tiles never mix requests)."""

@@ -190,3 +190,16 @@ def test_bench_pair_counts_match_the_oracle():
         [47929, 95425, 95425, 142921]
     cu = oracle.cu_seqlens_from_lengths([17, 0, 64, 129, 1])
     assert bench.varlen_pairs(cu) == int(np.count_nonzero(oracle.block_diagonal_mask(cu, cu)))
+
+
+def test_validate_cu_seqlens_host_check():
+    """The binding's opt-in host check of cu_seqlens (the kernels take them on
+    trust): accepts well-formed arrays, rejects the malformed ones."""
+    vl.validate_cu_seqlens([0, 17, 81, 210], rows=210, max_len=129)
+    vl.validate_cu_seqlens([0, 0, 5, 5], rows=8, max_len=5)          # empty requests, rows to spare
+    for bad, rows, max_len in (([], 10, 10), ([1, 5], 10, 10),        # empty / not starting at 0
+                               ([0, 5, 4], 10, 10),                     # decreasing
+                               ([0, 5, 11], 10, 10),                    # past the packed rows
+                               ([0, 5, 10], 10, 4)):                    # longer than the launch bound
+        with pytest.raises(vl.VarlenError):
+            vl.validate_cu_seqlens(bad, rows=rows, max_len=max_len)
