@@ -1267,9 +1267,11 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
 // a half read one 128-byte row segment).  Against tiles of 128 rows over the
 // union of their rows' windows this cuts the fp32 MFMA work 2-4.5x at the
 // Token2Wav shape (24-frame blocks).
-//   S^T = K Q^T with v_mfma_f32_32x32x2_f32: lane (ql, g) holds features
-//   [32g, 32g + 32) of query row ql (B operand) and of key row ql of the
-//   chunk (A operand); step s contracts feature 32g + s of both halves.  The
+//   S^T = K Q^T with v_mfma_f32_32x32x2_f32: lane (ql, g) holds the 16-byte
+//   chunks 2i + g (features 8i + 4g .. +3, i = 0..7) of query row ql (B
+//   operand) and of key row ql of the chunk (A operand), so the two halves of
+//   a load read the same 128-byte lines; step 4i + e contracts feature
+//   8i + 4g + e of both halves.  The
 //   result gives lane (ql, g) the scores of query ql for keys score_key(0, j, g).
 //   O^T += V^T P^T: step j contracts key score_key(0, j, g) of each half, whose
 //   probability is the lane's own score register j (see the tiled kernel).
@@ -1303,10 +1305,10 @@ __global__ void __launch_bounds__(256) block_local_f32_kernel(AttnArgs a) {
   // query rows past the block's end repeat its last row (computed, not stored)
   float qf[NQ];
   {
-    const float* qp = qg + base + (int64_t)(r0 + min(ql, nq - 1)) * row_stride + g * NQ;
+    const float* qp = qg + base + (int64_t)(r0 + min(ql, nq - 1)) * row_stride + 4 * g;
 #pragma unroll
     for (int s4 = 0; s4 < NQ / 4; ++s4) {
-      const f32x4 x = *(const f32x4*)(qp + 4 * s4);
+      const f32x4 x = *(const f32x4*)(qp + 8 * s4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf[4 * s4 + e] = x[e];
     }
@@ -1318,10 +1320,10 @@ __global__ void __launch_bounds__(256) block_local_f32_kernel(AttnArgs a) {
     // keys past the window's end read its last row (finite; masked below)
     float kf[NQ];
     {
-      const float* kp = kg + base + (int64_t)min(key0 + ql, k_hi - 1) * row_stride + g * NQ;
+      const float* kp = kg + base + (int64_t)min(key0 + ql, k_hi - 1) * row_stride + 4 * g;
 #pragma unroll
       for (int s4 = 0; s4 < NQ / 4; ++s4) {
-        const f32x4 x = *(const f32x4*)(kp + 4 * s4);
+        const f32x4 x = *(const f32x4*)(kp + 8 * s4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) kf[4 * s4 + e] = x[e];
       }
