@@ -3,8 +3,10 @@
  *
  * All tensor pointers are DEVICE pointers owned by the caller.  Every function
  * enqueues its work on `stream` and returns at once: no allocation, no
- * host<->device copy or synchronisation.  The only state the library keeps is
- * a per-device cache of one occupancy query (varlen_attn_fwd_split).  Device-
+ * host<->device copy or synchronisation.  The library keeps no global mutable
+ * state with one exception: a per-device cache of one occupancy query
+ * (resident work-groups of the attention kernel, read once, mutex-guarded),
+ * which sizes the key split of varlen_attn_fwd_split.  Device-
  * resident cu_seqlens are trusted preconditions (checking them would need a
  * device-to-host read); host scalars are validated and a bad one returns an
  * error code before anything is launched.  Return value: VL_OK (0) on success,
@@ -232,6 +234,10 @@ int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chu
                          int64_t max_chunks, int64_t* chunk_size, int64_t* chunk_count);
 
 /* ---------------------------------------------------------------- schedule (test export)
+ * The tile map serves the contract that no token attends across request
+ * boundaries (PR #4024, "Correctness model"; PR #6711, "Key changes": one
+ * flat pass over the packed batch): every work item lies inside one request
+ * and one head, so the attention kernels never mix requests.
  * varlen_launch_shape: host-only; the launch varlen_attn_fwd (dtype_f32 = 0,
  *   split = 0), varlen_attn_fwd_split (dtype_f32 = 0, split = 1) or
  *   varlen_attn_fwd_f32 (dtype_f32 = 1) uses for these scalars: query rows

@@ -130,9 +130,9 @@ def pack_by_cu_seqlens(src_padded, cu_seqlens, dst_rows: Optional[int] = None,
                        dst_row_offsets=None, dst=None) -> np.ndarray:
     """Gather only the real rows of a padded per-request buffer into a flat one.
 
-    PR #4024 "How batching works": instead of padding every request to the
-    largest shape, only real tokens are packed, and padded tokens never enter
-    the attention path.  src_padded has shape [R, S, ...]; request r has
+    PR #4024 "How batching works": a batch is formed from each request's
+    real tokens alone, with no padding to a common length, so pad rows never
+    reach attention.  src_padded has shape [R, S, ...]; request r has
     len_r = cu[r+1] - cu[r] real rows at src[r, 0:len_r].  They go to
     dst[off_r + i] with off_r = dst_row_offsets[r] if given, else cu[r].
     Rows of dst that no request writes keep their previous content (dst given)

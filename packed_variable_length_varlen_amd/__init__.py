@@ -286,10 +286,10 @@ def _attn_prep(q, k, v, dtype):
 
 def validate_cu_seqlens(cu, rows: int, max_len: int, what: str = "cu_seqlens") -> None:
     """Host-side check of a cu_seqlens array the kernels take on trust:
-    cu[0] = 0, non-decreasing, cu[-1] <= rows (the packed tensor's rows), and
-    every length <= max_len (the bound that sized the launch).  Raises
-    VarlenError.  `cu` is a sequence of ints or a tensor (copied to the host,
-    which synchronises with the device)."""
+    cu[0] = 0, non-decreasing, cu[-1] == rows (padded_tokens = 0: every row of
+    the packed tensor belongs to a request), and every length <= max_len (the
+    bound that sized the launch).  Raises VarlenError.  `cu` is a sequence of
+    ints or a tensor (copied to the host, which synchronises with the device)."""
     c = [int(x) for x in (cu.tolist() if isinstance(cu, torch.Tensor) else cu)]
     if not c or c[0] != 0:
         raise VarlenError(f"{what}[0] must be 0")
@@ -298,8 +298,9 @@ def validate_cu_seqlens(cu, rows: int, max_len: int, what: str = "cu_seqlens") -
             raise VarlenError(f"{what} must be non-decreasing ({what}[{i + 1}] < {what}[{i}])")
         if c[i + 1] - c[i] > max_len:
             raise VarlenError(f"request {i} has {c[i + 1] - c[i]} rows, more than the bound {max_len}")
-    if c[-1] > rows:
-        raise VarlenError(f"{what}[-1] = {c[-1]} exceeds the {rows} rows of the packed tensor")
+    if c[-1] != rows:
+        raise VarlenError(f"{what}[-1] = {c[-1]} differs from the {rows} rows of the packed tensor "
+                          f"(padded_tokens must be 0)")
 
 
 def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse, padded_tokens,
@@ -404,10 +405,14 @@ def _block_local(fn_name, dtype, q, k, v, block, look_back, look_ahead, scale, o
     if out is None:
         out = torch.empty_like(q)
     _gpu(out, "out", dtype)
+    if out.shape != q.shape:
+        raise VarlenError("out must have the shape of q")
     if lse is None and return_lse:
         lse = torch.empty((B, n, H), dtype=torch.float32, device=q.device)
     if lse is not None:
         _gpu(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, n, H):
+            raise VarlenError("lse must be [batch, frames, heads]")
     rc = getattr(load_library(), fn_name)(_ptr(q), _ptr(k), _ptr(v), B, n, H, D, int(block), int(look_back),
                                           int(look_ahead), float(scale), _ptr(out), _ptr(lse),
                                           _stream(stream))

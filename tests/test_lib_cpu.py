@@ -196,10 +196,11 @@ def test_validate_cu_seqlens_host_check():
     """The binding's opt-in host check of cu_seqlens (the kernels take them on
     trust): accepts well-formed arrays, rejects the malformed ones."""
     vl.validate_cu_seqlens([0, 17, 81, 210], rows=210, max_len=129)
-    vl.validate_cu_seqlens([0, 0, 5, 5], rows=8, max_len=5)          # empty requests, rows to spare
+    vl.validate_cu_seqlens([0, 0, 5, 5], rows=5, max_len=5)          # empty requests
     for bad, rows, max_len in (([], 10, 10), ([1, 5], 10, 10),        # empty / not starting at 0
                                ([0, 5, 4], 10, 10),                     # decreasing
                                ([0, 5, 11], 10, 10),                    # past the packed rows
+                               ([0, 0, 5, 5], 8, 5),                    # rows no request covers
                                ([0, 5, 10], 10, 4)):                    # longer than the launch bound
         with pytest.raises(vl.VarlenError):
             vl.validate_cu_seqlens(bad, rows=rows, max_len=max_len)

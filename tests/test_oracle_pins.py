@@ -29,6 +29,74 @@ def _np(t):
 # ---------------------------------------------------------------- integers
 
 
+def _validator_pins(validate):
+    """What the flat branch's boundary contract fixes (PR #6711, "Reference /
+    Acknowledgement": q/kv cu_seqlens with max lengths and padded_tokens = 0):
+    a well-formed array is accepted unchanged, and each way of breaking the
+    contract is refused."""
+    assert list(validate([0, 17, 81, 210], total=210, max_len=129)) == [0, 17, 81, 210]
+    assert list(validate([0, 0, 5, 5], total=5, max_len=5)) == [0, 0, 5, 5]  # empty requests
+    assert list(validate([0])) == [0]                                        # no request at all
+    with pytest.raises(ValueError):
+        validate([1, 17, 81, 210])                  # does not start at 0
+    with pytest.raises(ValueError):
+        validate([0, 17, 16, 210])                  # decreasing
+    with pytest.raises(ValueError):
+        validate([0, 17, 81, 211], total=210)       # rows past the last request (padding)
+    with pytest.raises(ValueError):
+        validate([0, 17, 81, 209], total=210)       # fewer rows than the tensor holds
+    with pytest.raises(ValueError):
+        validate([0, 17, 81, 210], max_len=128)     # a request over the declared max
+    with pytest.raises(ValueError):
+        validate([])                                # not num_reqs + 1 entries
+    with pytest.raises(ValueError):
+        validate([[0, 1], [1, 2]])                  # not 1-D
+
+
+def test_validate_cu_seqlens_accepts_the_contract_and_refuses_the_rest():
+    _validator_pins(vo.validate_cu_seqlens)
+
+
+def test_varlen_attention_refuses_malformed_boundaries():
+    q, k, v = (_np(t) for t in wl.random_varlen_case(5, [3, 4], 1, 4, torch.float32))
+    good = [0, 3, 7]
+    oracle.varlen_attention(q, k, v, good, good, 0.5)
+    for bad in ([0, 8, 7], [1, 3, 7], [0, 3, 6], [0, 3, 8]):
+        with pytest.raises(ValueError):
+            oracle.varlen_attention(q, k, v, bad, good, 0.5)
+        with pytest.raises(ValueError):
+            oracle.varlen_attention(q, k, v, good, bad, 0.5)
+
+
+def _planted_validator(old: str, new: str):
+    """validate_cu_seqlens with one line of its source replaced (a planted slip)."""
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(vo.validate_cu_seqlens))
+    assert old in src
+    ns = dict(vo.__dict__)
+    exec(compile(src.replace(old, new), "<planted>", "exec"), ns)
+    return ns["validate_cu_seqlens"]
+
+
+@pytest.mark.parametrize("old,new", [
+    ("np.any(lengths < 0)", "False"),                     # monotonicity check skipped
+    ("cu[0] != 0", "False"),                              # start not checked
+    ("cu[-1] != total", "cu[-1] > total"),                # padding rows let through
+    ("lengths.max() > max_len", "lengths.max() > max_len + 1"),  # max off by one
+])
+def test_planted_validator_slips_are_caught(monkeypatch, old, new):
+    bad = _planted_validator(old, new)
+    with pytest.raises(pytest.fail.Exception):
+        _validator_pins(bad)
+    # the attention oracle looks the validator up at call time, so the slip
+    # reaches it too and the refusal test catches it there as well
+    if old == "np.any(lengths < 0)":
+        monkeypatch.setattr(vo, "validate_cu_seqlens", bad)
+        with pytest.raises(pytest.fail.Exception):
+            test_varlen_attention_refuses_malformed_boundaries()
+
+
 def test_text_mask_lengths_count_true_entries():
     rng = np.random.default_rng(0)
     lengths = rng.integers(0, 257, size=9)
