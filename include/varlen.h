@@ -199,6 +199,26 @@ int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int
                           void* workspace, int64_t workspace_bytes, vl_stream_t stream);
 int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, int32_t D, int64_t* bytes);
 
+/* varlen_attn_fwd_noalloc: for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc).  Same arguments and contract as varlen_attn_fwd; it runs the
+ *   key split of the last round like varlen_attn_fwd_split, with the same
+ *   split plan, but keeps the partial results in a static device array of
+ *   VL_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends) and reads V
+ *   row-major (no V^T staging, whose buffer grows with the input); its out and
+ *   lse are the same bits as varlen_attn_fwd_split's.  It calls no hipMalloc
+ *   or hipFree.  The partials need slots * 256 * (4 * D + 8) bytes, slots =
+ *   the attention kernel's resident work-groups on the device (256 on an
+ *   MI355X: 34 MB at D = 128); a device needing more returns VL_EUNSUPPORTED.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (two streams, two threads) race and must be ordered by the caller.
+ *   The array needs no clearing: each call writes every partial it reads.
+ */
+#define VL_NOALLOC_SCRATCH_BYTES (48 * 1024 * 1024)
+int varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
+                            const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
+                            int32_t H, int32_t D, float scale, void* out, float* lse, vl_stream_t stream);
+
 /* ---------------------------------------------------------------- block-local attention
  * block_local_attn_fwd: the block-local ("block-sparse") attention of the
  *   Token2Wav DiT (PR #7975, review of the window code, commit messages,

@@ -19,7 +19,7 @@ __all__ = [
     "load_library", "lib_path", "cu_seqlens_from_lengths", "joint_cu_seqlens",
     "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "pack_by_cu_seqlens_batched",
     "unpack_by_cu_seqlens_batched", "varlen_attn_fwd", "varlen_attn_fwd_split",
-    "varlen_split_workspace_bytes", "varlen_attn_fwd_f32",
+    "varlen_split_workspace_bytes", "varlen_attn_fwd_f32", "varlen_attn_fwd_noalloc",
     "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
     "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError", "validate_cu_seqlens",
 ]
@@ -52,6 +52,8 @@ _SIGNATURES = {
     "varlen_attn_fwd_split": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                _vp, _vp, _c_i64, _vp, _c_i64, _vp], _c_int),
     "varlen_split_workspace_bytes": ([_c_i64, _c_i32, _c_i32, _c_i32, _vp], _c_int),
+    "varlen_attn_fwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                 _vp, _vp, _vp], _c_int),
     "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _vp, _vp, _vp],
                             _c_int),
     "varlen_tile_map": ([_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _c_i64, _vp],
@@ -382,6 +384,18 @@ def varlen_attn_fwd_split(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, s
     is allocated when not given."""
     return _varlen("varlen_attn_fwd_split", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
                    max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace,
+                   check_cu_seqlens=check_cu_seqlens)
+
+
+def varlen_attn_fwd_noalloc(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, scale=None, out=None,
+                            lse=None, padded_tokens: int = 0, attn_mask=None, return_lse: bool = False,
+                            stream=None, check_cu_seqlens: bool = False):
+    """varlen_attn_fwd with the key split of the last round and no device
+    allocation in the library: the split's partial results live in a static
+    device array (one per GPU; overlapping calls on one GPU race).  out / lse
+    are allocated here only when not given."""
+    return _varlen("varlen_attn_fwd_noalloc", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
+                   max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream,
                    check_cu_seqlens=check_cu_seqlens)
 
 

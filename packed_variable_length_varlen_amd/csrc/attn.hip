@@ -1699,11 +1699,38 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? VL_OK : VL_ELAUNCH;
 }
 
+// Device scratch of the allocation-free varlen entry point: the partial
+// results of the key split (split_partial_bytes(slots, D)).  Every GPU the
+// library runs on holds one copy until the process ends; host code never
+// passes the array's name to a kernel (on the host it is only a stand-in) but
+// the device address looked up once per device by noalloc_scratch().
+static __device__ __align__(256) char scratch[VL_NOALLOC_SCRATCH_BYTES];
+
+// Address of this device's `scratch`, looked up with the device current on
+// the first call on that device; nullptr if the lookup fails.
+void* noalloc_scratch(int dev) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+// split: the key split of the last round, with the workspace (V^T staged
+// there, partials after it) or, when noalloc, with the partials in the
+// device's `scratch` and V read row-major.
 template <bool kF32>
 int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_cu,
                   const int32_t* kv_cu, int32_t max_q, int32_t max_kv, int32_t num_reqs,
                   int32_t H, int32_t D, float scale, void* out, float* lse, bool split, int64_t kv_rows,
-                  void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                  void* workspace, int64_t workspace_bytes, hipStream_t stream, bool noalloc = false) {
   if (num_reqs < 0 || max_q < 0 || max_kv < 0 || H < 1 || kv_rows < 0) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
   if (num_reqs == 0 || max_q == 0) return VL_OK;
@@ -1716,12 +1743,25 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   const VarlenPlan plan = varlen_plan(kF32, split, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
-  // the split launch stages V^T; its copies address a head's V^T with 32-bit offsets
-  const int64_t vt_ld = split ? vl::vt_row_len(kv_rows, num_reqs) : 0;
-  if (split && ((int64_t)D * vt_ld * 2 > INT32_MAX || vt_ld / vl::kVtTile * H > INT32_MAX)) return VL_EUNSUPPORTED;
-  if (split && (!workspace || !aligned16(workspace) ||
-                workspace_bytes < split_workspace_bytes(plan.slots, kv_rows, num_reqs, H, D)))
+  // the workspace launch stages V^T; its copies address a head's V^T with 32-bit offsets
+  const bool stage_vt = split && !noalloc;
+  const int64_t vt_ld = stage_vt ? vl::vt_row_len(kv_rows, num_reqs) : 0;
+  if (stage_vt && ((int64_t)D * vt_ld * 2 > INT32_MAX || vt_ld / vl::kVtTile * H > INT32_MAX))
+    return VL_EUNSUPPORTED;
+  if (stage_vt && (!workspace || !aligned16(workspace) ||
+                   workspace_bytes < split_workspace_bytes(plan.slots, kv_rows, num_reqs, H, D)))
     return VL_EINVAL;
+  if (noalloc) {
+    // the partials must fit the static scratch; its address is this device's
+    if (split_partial_bytes(plan.slots, D) > (int64_t)VL_NOALLOC_SCRATCH_BYTES) return VL_EUNSUPPORTED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+      (void)hipGetLastError();
+      return VL_ELAUNCH;
+    }
+    workspace = plan.slots > 0 ? noalloc_scratch(dev) : nullptr;
+    if (plan.slots > 0 && workspace == nullptr) return VL_ELAUNCH;
+  }
   vl::AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -1737,7 +1777,7 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   a.slots = plan.slots;
   a.max_kv = max_kv;
   a.ws = (float*)workspace;
-  if (split) {
+  if (stage_vt) {
     a.vt = (char*)workspace + split_partial_bytes(plan.slots, D);
     a.vt_ld = vt_ld;
   }
@@ -1749,7 +1789,7 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
     return launch_status();
   }
-  if (split) {
+  if (stage_vt) {
     const unsigned tb = (unsigned)(vt_ld / vl::kVtTile * H);
     if (D == 128) {
       hipLaunchKernelGGL((vl::vt_transpose_kernel<128>), dim3(tb), dim3(256), 0, stream, a);
@@ -1856,6 +1896,13 @@ int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int
                           void* workspace, int64_t workspace_bytes, vl_stream_t stream) {
   return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
                               scale, out, lse, true, kv_rows, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* q_cu_seqlens,
+                            const int32_t* kv_cu_seqlens, int32_t max_q, int32_t max_kv, int32_t num_reqs,
+                            int32_t H, int32_t D, float scale, void* out, float* lse, vl_stream_t stream) {
+  return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
+                              scale, out, lse, true, 0, nullptr, 0, (hipStream_t)stream, true);
 }
 
 int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, int32_t D, int64_t* bytes) {
