@@ -10,14 +10,25 @@ One step = one pass of the whole path over one batch of synthetic input:
   5. block-local attention of the vocoder-DiT shape (n=2003, 24-frame blocks,
      H=16, D=64) for each of the four window types (own block, one back,
      one ahead, both).
-The default workload is the single joint request of a 2048x2048 image
-(16,384 image tokens + 8..256 text tokens, H=24, D=128, bf16).
+The default workload is the largest single-GPU one: the edit-style batch of
+four CFG sequences [r1+, r1-, r2+, r2-], each 32,768 image tokens (noise +
+source latents) after its text (about 131.5k packed tokens, H=24, D=128,
+bf16).  Every input is drawn by the seeded NumPy recipe of workloads.py (the
+same bits the parity tests check) and is resident in HBM before timing.
 
 value = algorithmic FLOP of one step / step time, where the FLOP count is
 4*D*H per in-request (query, key) pair (the varlen pairs plus the in-window
 block-local pairs); work the kernels avoid is never counted.
 
-Prints ONE JSON line on stdout; details go to stderr.
+The `detail` object holds the same step at the two other full-size workloads,
+the bandwidth-bound pieces alone (warm and with the last-level cache flushed),
+the block-local calls per window and weighted by the DiT's layer mix, the
+production block-local shape, the fused CFG combine, and the launch floor.
+The CPU baseline is the fp64 oracle run by a process pool (one BLAS thread per
+worker) on a bounded sample of the headline workload's (request, head, query
+rows) units; its rate is extrapolated to the whole workload.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
 """
 
 from __future__ import annotations
@@ -25,6 +36,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import multiprocessing as mp
 import os
 import sys
 import time
@@ -37,6 +49,7 @@ PROFILES = os.path.join(HERE, "profiles")
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BOX_CPU_SHARE = 16          # worker processes at most (the CPU share of one GPU)
 
 
 def err(*a):
@@ -52,8 +65,8 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch of the attention kernel from committed rocprofv3
-    --pmc counters (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel factor);
+    """HBM bytes per attention call from committed rocprofv3 --pmc counters
+    (FETCH_SIZE + WRITE_SIZE of its kernels, scaled by a copy-kernel factor);
     None when absent or taken on a different kernel source."""
     path = os.path.join(PROFILES, "varlen_attn_bf16_traffic.json")
     if not os.path.exists(path):
@@ -81,16 +94,51 @@ def block_local_pairs(n: int, block: int, lb: int, la: int) -> int:
     return tot
 
 
-def cpu_baseline(inp, cu_host, budget_s: float = 15.0):
-    """Time the CPU oracle on a bounded sample of the same workload: query rows
-    of the varlen attention, taken in blocks of 128 until ~budget_s has passed.
-    Returns the oracle's throughput in TFLOP/s (same 4*D*H per pair count)."""
-    import oracle  # the reported CPU baseline only
+# ------------------------------------------------------------------ CPU baseline (oracle, process pool)
+
+# Packed fp64 q/k/v and boundaries of the workload the pool samples.  Set in
+# the parent before the pool is forked (before any GPU use), so the workers
+# share them copy-on-write and receive only indices.
+_ORACLE = {}
+
+
+def _oracle_worker_init():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:
-        cores = os.cpu_count() or 1
+        pass
+
+
+def _oracle_task(task):
+    """One unit of the sample: query rows [a, b) of request r, head h, against
+    the request's keys (rows are independent, so a subset is exact)."""
+    import oracle
+    r, h, a, b = task
+    d = _ORACLE
+    cu = d["cu"]
+    k0, k1 = int(cu[r]), int(cu[r + 1])
+    q = d["q"][int(cu[r]) + a:int(cu[r]) + b, h:h + 1]
+    k = d["k"][k0:k1, h:h + 1]
+    v = d["v"][k0:k1, h:h + 1]
+    oracle.varlen_attention(q, k, v, [0, b - a], [0, k1 - k0], d["scale"])
+    return 4.0 * q.shape[2] * (b - a) * (k1 - k0)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def prepare_oracle_pool(inp):
+    """Pack the workload for the oracle (fp64) and fork the worker pool."""
+    import oracle
     H, D = inp.spec.H, inp.spec.D
     cj, ct, ci, idst = oracle.joint_cu_seqlens(inp.text_mask, inp.img_hw)
     T = int(cj[-1])
@@ -99,23 +147,145 @@ def cpu_baseline(inp, cu_host, budget_s: float = 15.0):
         dst = np.zeros((T, H, D), dtype=np.float32)
         oracle.pack_by_cu_seqlens(txt.float().numpy(), ct, dst_row_offsets=cj[:-1], dst=dst)
         oracle.pack_by_cu_seqlens(img.float().numpy(), ci, dst_row_offsets=idst, dst=dst)
-        packed.append(dst)
-    q, k, v = packed
+        packed.append(dst.astype(np.float64))
+        del dst
+    _ORACLE.update(q=packed[0], k=packed[1], v=packed[2], cu=cj, scale=inp.scale, H=H, D=D)
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    workers = max(1, min(BOX_CPU_SHARE, share))
+    pool = mp.get_context("fork").Pool(workers, initializer=_oracle_worker_init)
+    return pool, workers, share
+
+
+def run_cpu_baseline(pool, workers: int, share: int, budget_s: float):
+    """Time the oracle on a bounded sample: (request, head, 256 query rows)
+    units dealt round-robin over requests and heads, submitted until about
+    budget_s of wall time has passed; rate = their FLOP / wall time."""
+    d = _ORACLE
+    cu = [int(x) for x in d["cu"]]
+    R, H, D = len(cu) - 1, d["H"], d["D"]
     rng = np.random.default_rng(0)
-    order = rng.permutation(T)
-    flops = 0.0
-    rows_done = 0
+    units = []
+    for i in range(R * H * 64):
+        r, h = (i // H) % R, i % H
+        L = cu[r + 1] - cu[r]
+        if L == 0:
+            continue
+        a = int(rng.integers(0, max(1, L - 256) + 1))
+        units.append((r, h, a, min(L, a + 256)))
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and rows_done < T:
-        rows = np.sort(order[rows_done:rows_done + 128])
-        oracle.varlen_attention(q, k, v, cj, cj, inp.scale, rows=rows)
-        req = np.searchsorted(cj, rows, side="right") - 1
-        flops += float(sum(4 * D * H * int(cj[r + 1] - cj[r]) for r in req))
-        rows_done += rows.size
+    pending, flops, done, it = [], 0.0, 0, iter(units)
+    for _ in range(2 * workers):
+        pending.append(pool.apply_async(_oracle_task, (next(it),)))
+    while pending:
+        res = pending.pop(0)
+        flops += res.get()
+        done += 1
+        if time.perf_counter() - t0 < budget_s:
+            nxt = next(it, None)
+            if nxt is not None:
+                pending.append(pool.apply_async(_oracle_task, (nxt,)))
     dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows_done} of {T} query rows x {H} heads of the varlen attention "
-                      f"(fp64 NumPy oracle, {dt:.1f} s)"}
+    pool.close()
+    pool.join()
+    total_flops = 4.0 * D * H * varlen_pairs(cu)
+    rate = flops / dt
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "sample": f"{done} units of (request, head, <=256 query rows) of the varlen attention, "
+                      f"{flops / 1e12:.3f} TFLOP in {dt:.1f} s on {workers} worker processes "
+                      f"(fp64 NumPy oracle, one BLAS thread each)",
+            "nproc": os.cpu_count(), "cpu_share": share, "cpu_model": cpu_model(),
+            "full_workload_oracle_s_extrapolated": round(total_flops / rate, 1)}
+
+
+# ------------------------------------------------------------------ GPU timing
+
+
+class VarlenStep:
+    """The varlen part of the step for one workload, inputs resident in HBM."""
+
+    def __init__(self, vl, wl, inp, dev):
+        self.vl, self.inp = vl, inp
+        H, D = inp.spec.H, inp.spec.D
+        R, T = inp.R, inp.total_tokens
+        self.H, self.D, self.R, self.T = H, D, R, T
+        self.max_len = inp.max_len
+        self.mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(dev)
+        self.hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=dev).reshape(R, 2)
+        self.slabs = [(t.to(dev), i.to(dev)) for t, i in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img),
+                                                          (inp.v_text, inp.v_img))]
+        self.cu_j = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        self.cu_t = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        self.cu_i = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        self.img_dst = torch.empty(R, dtype=torch.int32, device=dev)
+        self.packed = [torch.empty((T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+        self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        self.out_txt = torch.empty_like(self.slabs[0][0])
+        self.out_img = torch.empty_like(self.slabs[0][1])
+        # workspace of the attention call (allocated once): staged V^T and the
+        # partial results of the key split of the last round
+        self.workspace = torch.empty(vl.varlen_split_workspace_bytes(T, R, H, D), dtype=torch.uint8, device=dev)
+        self.pack_items = []
+        for (txt, img), dst in zip(self.slabs, self.packed):
+            self.pack_items += [(txt, self.cu_t, dst, self.cu_j[:-1]), (img, self.cu_i, dst, self.img_dst)]
+        self.unpack_items = [(self.out, self.cu_t, self.out_txt, self.cu_j[:-1]),
+                             (self.out, self.cu_i, self.out_img, self.img_dst)]
+        row_bytes = H * D * 2
+        real_rows = sum(inp.text_len) + sum(inp.img_tokens)
+        self.pack_bytes = 3 * 2 * real_rows * row_bytes
+        self.unpack_bytes = real_rows * row_bytes + R * (wl.TEXT_CAP + inp.img_cap) * row_bytes
+
+    def cu(self):
+        self.vl.joint_cu_seqlens(self.mask_d, self.hw_d, outs=(self.cu_j, self.cu_t, self.cu_i, self.img_dst))
+
+    def pack(self):
+        self.vl.pack_by_cu_seqlens_batched(self.pack_items)
+
+    def attention(self):
+        q, k, v = self.packed
+        self.vl.varlen_attn_fwd_split(q, k, v, self.cu_j, self.cu_j, self.max_len, self.max_len, self.inp.scale,
+                                      out=self.out, workspace=self.workspace)
+
+    def unpack(self):
+        self.vl.unpack_by_cu_seqlens_batched(self.unpack_items)
+
+    def pairs(self) -> int:
+        return varlen_pairs(self.cu_j.cpu().numpy())
+
+
+def new_event(stream):
+    e = torch.cuda.Event(enable_timing=True)
+    e.record(stream)
+    return e
+
+
+def time_steps(stream, parts, steps: int, warmup: int):
+    """Runs `steps` steps of the callables in `parts` (name, fn or None =
+    untimed) after `warmup` untimed steps.  Returns (wall seconds of the timed
+    steps, {name: mean ms per step from the HIP events around it})."""
+    def step(record):
+        evs = []
+        for name, fn in parts:
+            e0 = new_event(stream) if record and name else None
+            fn()
+            if e0 is not None:
+                evs.append((name, e0, new_event(stream)))
+        return evs
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = [step(True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = {}
+    for evs in recs:
+        for name, a, b in evs:
+            ms.setdefault(name, []).append(a.elapsed_time(b))
+    return dt, {k: float(np.mean(v)) for k, v in ms.items()}
 
 
 def main():
@@ -123,10 +293,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="joint-16k", choices=["joint-16k", "mixres-4req", "edit-cfg-4seq"])
+    ap.add_argument("--workload", default="edit-cfg-4seq", choices=["joint-16k", "mixres-4req", "edit-cfg-4seq"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle sampling")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="only the timed steps (profiling runs: one workload's launches per trace)")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the attention timings at the other full-size workloads (profiling runs)")
+                    help="skip the steps at the other full-size workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -149,268 +322,213 @@ def main():
     import packed_variable_length_varlen_amd as vl
     from packed_variable_length_varlen_amd import workloads as wl
 
-    vl.load_library()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
+    # ---- inputs, drawn on the host by the seeded recipe (before any GPU use)
     spec = wl.WORKLOADS[args.workload]
     err(f"[bench] generating {args.workload} ({spec.name})")
     inp = wl.make_varlen_inputs(spec, torch.bfloat16)
-    H, D = spec.H, spec.D
-    R = inp.R
-    T = inp.total_tokens
-    max_len = inp.max_len
-
-    # inputs resident in HBM before timing
-    mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(dev)
-    hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=dev).reshape(R, 2)
-    slabs = [(t.to(dev), i.to(dev)) for t, i in ((inp.q_text, inp.q_img), (inp.k_text, inp.k_img),
-                                                  (inp.v_text, inp.v_img))]
-    cu_j = torch.empty(R + 1, dtype=torch.int32, device=dev)
-    cu_t = torch.empty(R + 1, dtype=torch.int32, device=dev)
-    cu_i = torch.empty(R + 1, dtype=torch.int32, device=dev)
-    img_dst = torch.empty(R, dtype=torch.int32, device=dev)
-    packed = [torch.empty((T, H, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-    out_txt = torch.empty_like(slabs[0][0])
-    out_img = torch.empty_like(slabs[0][1])
-
-    # workspace of the attention call (allocated once): staged V^T and the
-    # partial results of the key split of the last round
-    workspace = torch.empty(vl.varlen_split_workspace_bytes(T, R, H, D), dtype=torch.uint8, device=dev)
-
+    others = []
+    if not (args.no_detail or args.no_other_workloads):
+        for name in ("joint-16k", "mixres-4req", "edit-cfg-4seq"):
+            if name != args.workload:
+                err(f"[bench] generating {name}")
+                others.append((name, wl.make_varlen_inputs(wl.WORKLOADS[name], torch.bfloat16)))
     bl_spec = wl.BLOCK_LOCAL_WORKLOADS["vocoder-dit"]
     bl = wl.make_block_local_inputs(bl_spec, torch.bfloat16)
+    pool = None
+    if not args.no_cpu_baseline:
+        err("[bench] packing the workload for the CPU oracle and forking its worker pool")
+        pool, workers, share = prepare_oracle_pool(inp)
+
+    # ---- GPU
+    vl.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    main_step = VarlenStep(vl, wl, inp, dev)
+    H, D, R, T = main_step.H, main_step.D, main_step.R, main_step.T
     bq, bk, bv = bl.q.to(dev), bl.k.to(dev), bl.v.to(dev)
     bouts = [torch.empty_like(bq) for _ in bl_spec.windows]
 
-    # the joint pack of Q, K, V (text and image pieces: six copies) and the
-    # unpack of the output (two copies), one launch each
-    pack_items = []
-    for (txt, img), dst in zip(slabs, packed):
-        pack_items += [(txt, cu_t, dst, cu_j[:-1]), (img, cu_i, dst, img_dst)]
-    unpack_items = [(out, cu_t, out_txt, cu_j[:-1]), (out, cu_i, out_img, img_dst)]
-
-    stream = torch.cuda.current_stream()
-    ev = {"attn": [], "pack": [], "unpack": [], "blocal": []}
-
-    def mark(record):
-        if not record:
-            return None
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        return e
-
-    def step(record: bool):
-        vl.joint_cu_seqlens(mask_d, hw_d, outs=(cu_j, cu_t, cu_i, img_dst))
-        e0 = mark(record)
-        vl.pack_by_cu_seqlens_batched(pack_items)
-        e1 = mark(record)
-        vl.varlen_attn_fwd_split(packed[0], packed[1], packed[2], cu_j, cu_j, max_len, max_len, inp.scale,
-                                 out=out, workspace=workspace)
-        e2 = mark(record)
-        vl.unpack_by_cu_seqlens_batched(unpack_items)
-        e3 = mark(record)
+    def block_local_all():
         for (lb, la), o in zip(bl_spec.windows, bouts):
             vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o)
-        e4 = mark(record)
-        if record:
-            ev["pack"].append((e0, e1))
-            ev["attn"].append((e1, e2))
-            ev["unpack"].append((e2, e3))
-            ev["blocal"].append((e3, e4))
 
-    err(f"[bench] T={T} R={R} H={H} D={D}: warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-
-    err(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
-    attn_ms = ms["attn"]
-    row_bytes = H * D * 2
-    real_rows = sum(inp.text_len) + sum(inp.img_tokens)
-    pack_bytes = 3 * 2 * real_rows * row_bytes
-    unpack_bytes = real_rows * row_bytes + R * (wl.TEXT_CAP + inp.img_cap) * row_bytes
-    err(f"[bench] pack q/k/v: {ms['pack']*1e3:.1f} us, {pack_bytes/ms['pack']/1e6:.0f} GB/s "
-        f"({100*pack_bytes/ms['pack']/1e6/HBM_PEAK_GBS:.1f}% of HBM); unpack out: {ms['unpack']*1e3:.1f} us, "
-        f"{unpack_bytes/ms['unpack']/1e6:.0f} GB/s ({100*unpack_bytes/ms['unpack']/1e6/HBM_PEAK_GBS:.1f}% of HBM); "
-        f"block-local x4: {ms['blocal']*1e3:.1f} us")
-
-    cu_host = cu_j.cpu().numpy()  # after timing: only for the FLOP count
-    pairs = varlen_pairs(cu_host)
+    parts = [(None, main_step.cu), ("pack", main_step.pack), ("attn", main_step.attention),
+             ("unpack", main_step.unpack), ("blocal", block_local_all)]
+    err(f"[bench] T={T} R={R} H={H} D={D}: warmup {args.warmup}, timing {args.steps} steps")
+    dt, ms = time_steps(stream, parts, args.steps, args.warmup)
+    pairs = main_step.pairs()
     bl_pairs = [block_local_pairs(bl_spec.n, bl_spec.block, lb, la) for lb, la in bl_spec.windows]
     flop_varlen = 4.0 * D * H * pairs
     flop_bl = 4.0 * bl_spec.D * bl_spec.H * sum(bl_pairs)
-    step_flop = flop_varlen + flop_bl
     ms_per_step = dt * 1e3 / args.steps
-    value = step_flop / (dt / args.steps) / 1e12
+    value = (flop_varlen + flop_bl) / (dt / args.steps) / 1e12
+    attn_ms = ms["attn"]
     achieved = flop_varlen / (attn_ms * 1e-3) / 1e12
-    workload = f"{spec.name}+{bl_spec.name}-4windows"
+    err(f"[bench] step {ms_per_step:.3f} ms = {value:.1f} TFLOP/s; attention {attn_ms:.3f} ms = "
+        f"{achieved:.1f} TFLOP/s ({100 * achieved / BF16_PEAK_TFLOPS:.1f}% of bf16 peak); "
+        f"pack {ms['pack'] * 1e3:.1f} us ({100 * main_step.pack_bytes / ms['pack'] / 1e6 / HBM_PEAK_GBS:.1f}% of HBM), "
+        f"unpack {ms['unpack'] * 1e3:.1f} us "
+        f"({100 * main_step.unpack_bytes / ms['unpack'] / 1e6 / HBM_PEAK_GBS:.1f}% of HBM), "
+        f"block-local x4 {ms['blocal'] * 1e3:.1f} us")
+
+    def step_record(s: VarlenStep, ms_, step_ms, pairs_):
+        fl = 4.0 * s.D * s.H * pairs_
+        return {"workload": s.inp.spec.name, "total_tokens": s.T, "requests": s.R, "in_request_pairs": pairs_,
+                "step_ms": round(step_ms, 4),
+                "attention_ms": round(ms_["attn"], 4), "attention_TFLOP/s": round(fl / ms_["attn"] / 1e9, 2),
+                "attention_pct_of_bf16_peak": round(100 * fl / ms_["attn"] / 1e9 / BF16_PEAK_TFLOPS, 2),
+                "pack_us": round(ms_["pack"] * 1e3, 2),
+                "pack_pct_of_hbm": round(100 * s.pack_bytes / ms_["pack"] / 1e6 / HBM_PEAK_GBS, 1),
+                "unpack_us": round(ms_["unpack"] * 1e3, 2),
+                "unpack_pct_of_hbm": round(100 * s.unpack_bytes / ms_["unpack"] / 1e6 / HBM_PEAK_GBS, 1)}
+
+    detail = {"steps": [step_record(main_step, ms, ms_per_step, pairs)]}
     traffic = load_traffic(args.workload)
 
-    err(f"[bench] step {ms_per_step:.3f} ms, attention {attn_ms:.3f} ms = {achieved:.1f} TFLOP/s "
-        f"({100 * achieved / BF16_PEAK_TFLOPS:.1f}% of bf16 peak); pairs {pairs}")
+    if not args.no_detail:
+        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
-    # Bandwidth-bound pieces in isolation: median / p10 / p90 of per-call event
-    # times, warm (calls back to back) and with the 256 MB last-level cache
-    # flushed before each call by reading a 512 MB buffer (a read leaves no
-    # dirty lines to be written back during the measured call).  All calls
-    # are enqueued before the one synchronisation, so no launch gap is timed.
-    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        def call_stats(fn, flushed: bool, reps: int = 30, warm: int = 5):
+            """median / p10 / p90 of per-call HIP event times (us); all calls are
+            enqueued before one synchronisation, so no launch gap is timed;
+            flushed: a 512 MB buffer is read before each call, so the 256 MB
+            last-level cache holds none of the call's data and no dirty lines."""
+            for _ in range(warm):
+                fn()
+            evs = []
+            for _ in range(reps):
+                if flushed:
+                    torch.sum(flush)
+                a = new_event(stream)
+                fn()
+                evs.append((a, new_event(stream)))
+            torch.cuda.synchronize()
+            t = [a.elapsed_time(b) * 1e3 for a, b in evs]
+            return [float(np.percentile(t, q)) for q in (50, 10, 90)]
 
-    def call_stats(fn, flushed: bool, reps: int = 30, warm: int = 5):
-        for _ in range(warm):
-            fn()
-        pairs_ev = []
-        for _ in range(reps):
-            if flushed:
-                torch.sum(flush)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            pairs_ev.append((a, b))
-        torch.cuda.synchronize()
-        times = [a.elapsed_time(b) * 1e3 for a, b in pairs_ev]  # us
-        return [float(np.percentile(times, q)) for q in (50, 10, 90)]
+        def bw_record(nbytes, fn):
+            rec = {"bytes": int(nbytes)}
+            for tag, fl in (("warm", False), ("flushed", True)):
+                med, p10, p90 = call_stats(fn, fl)
+                rec[tag] = {"us_median": round(med, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                            "GB/s": round(nbytes / med / 1e3, 1),
+                            "pct_of_hbm": round(100 * nbytes / med / 1e3 / HBM_PEAK_GBS, 1)}
+            return rec
 
-    def bw(nbytes, us):
-        return round(nbytes / us / 1e3, 1)  # GB/s
+        # the other full-size workloads: the same step (without the block-local
+        # calls), then their pack / unpack alone
+        steps_all = [main_step]
+        for name, oinp in others:
+            err(f"[bench] step at {name}")
+            s = VarlenStep(vl, wl, oinp, dev)
+            odt, oms = time_steps(stream, [(None, s.cu), ("pack", s.pack), ("attn", s.attention),
+                                           ("unpack", s.unpack)], max(10, args.steps // 2), 3)
+            detail["steps"].append(step_record(s, oms, odt * 1e3 / max(10, args.steps // 2), s.pairs()))
+            err(f"[bench]   attention {oms['attn']:.3f} ms = {detail['steps'][-1]['attention_TFLOP/s']} TFLOP/s "
+                f"({detail['steps'][-1]['attention_pct_of_bf16_peak']}%)")
+            steps_all.append(s)
 
-    detail = {}
-    for name, fn, nbytes in (("pack", lambda: vl.pack_by_cu_seqlens_batched(pack_items), pack_bytes),
-                             ("unpack", lambda: vl.unpack_by_cu_seqlens_batched(unpack_items), unpack_bytes)):
-        rec = {"bytes": int(nbytes)}
-        for tag, fl in (("warm", False), ("flushed", True)):
-            med, p10, p90 = call_stats(fn, fl)
-            rec[tag] = {"us_median": round(med, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2),
-                        "GB/s": bw(nbytes, med), "pct_of_hbm": round(100 * nbytes / med / 1e3 / HBM_PEAK_GBS, 1)}
-        detail[name] = rec
-        err(f"[bench] {name}: warm {rec['warm']['pct_of_hbm']}% / flushed {rec['flushed']['pct_of_hbm']}% of HBM")
-    # block-local, one call per window type: % of MFMA peak as the metric asks,
-    # and % of HBM over its unique bytes (q, k, v read, out written) as the roofline
-    bl_bytes = 4 * bl_spec.B * bl_spec.n * bl_spec.H * bl_spec.D * 2
-    detail["block_local"] = []
-    for (lb, la), o, npairs in zip(bl_spec.windows, bouts, bl_pairs):
-        med, p10, p90 = call_stats(lambda: vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o),
-                                   True)
-        fl = 4.0 * bl_spec.D * bl_spec.H * npairs
-        detail["block_local"].append({"look_back": lb, "look_ahead": la, "us_median": round(med, 2),
-                                      "us_p10": round(p10, 2), "us_p90": round(p90, 2),
-                                      "TFLOP/s": round(fl / med / 1e6, 2),
-                                      "pct_of_bf16_peak": round(100 * fl / med / 1e6 / BF16_PEAK_TFLOPS, 3),
-                                      "pct_of_hbm_unique_bytes": round(100 * bl_bytes / med / 1e3 / HBM_PEAK_GBS, 1)})
-    err(f"[bench] block-local (flushed) us: {[d['us_median'] for d in detail['block_local']]}")
-    # block-local at the DiT vocoder's production shape: CFG as batch 2, 4000
-    # frames (167 blocks, the last of 16), own-block and one-neighbour windows,
-    # in the pages' fp32 and in bf16
-    prod_n, prod_b = 4000, 2
-    detail["block_local_production"] = []
-    for pdt in (torch.float32, torch.bfloat16):
-        pin = wl.make_block_local_inputs(bl_spec, pdt, n=prod_n, B=prod_b, seed=prod_n)
-        pq, pk, pv = pin.q.to(dev), pin.k.to(dev), pin.v.to(dev)
-        po = torch.empty_like(pq)
-        fn = vl.block_local_attn_fwd_f32 if pdt == torch.float32 else vl.block_local_attn_fwd
-        pbytes = 4 * prod_b * prod_n * bl_spec.H * bl_spec.D * pq.element_size()
-        for lb, la in ((0, 0), (1, 0), (0, 1)):
-            med, p10, p90 = call_stats(lambda: fn(pq, pk, pv, bl_spec.block, lb, la, pin.scale, out=po), True)
-            fl = 4.0 * bl_spec.D * bl_spec.H * prod_b * block_local_pairs(prod_n, bl_spec.block, lb, la)
-            detail["block_local_production"].append({
-                "dtype": "f32" if pdt == torch.float32 else "bf16", "B": prod_b, "n": prod_n,
-                "look_back": lb, "look_ahead": la, "us_median": round(med, 2), "us_p10": round(p10, 2),
-                "us_p90": round(p90, 2), "TFLOP/s": round(fl / med / 1e6, 2),
-                "pct_of_hbm_unique_bytes": round(100 * pbytes / med / 1e3 / HBM_PEAK_GBS, 1)})
-        del pq, pk, pv, po, pin
-    err(f"[bench] block-local production (flushed) us: "
-        f"{[(d['dtype'], d['look_back'], d['look_ahead'], d['us_median']) for d in detail['block_local_production']]}")
+        detail["copies_alone"] = []
+        for s in steps_all:
+            for what, fn, nbytes in (("pack", s.pack, s.pack_bytes), ("unpack", s.unpack, s.unpack_bytes)):
+                rec = {"workload": s.inp.spec.name, "copy": what, **bw_record(nbytes, fn)}
+                detail["copies_alone"].append(rec)
+                err(f"[bench] {what} at {s.inp.spec.name}: warm {rec['warm']['pct_of_hbm']}% / "
+                    f"flushed {rec['flushed']['pct_of_hbm']}% of HBM")
 
-    # The attention call alone at the other full-size workloads (same launch,
-    # per-call HIP events, median of 10): their token layout from the recipe's
-    # text-length draws, Q/K/V N(0,1) drawn on the device (seeded).
-    detail["attention_other_workloads"] = []
-    for other in ("joint-16k", "mixres-4req", "edit-cfg-4seq"):
-        if other == args.workload or args.no_other_workloads:
-            continue
-        ospec = wl.WORKLOADS[other]
-        lens = wl.varlen_lengths(ospec)
-        oT = sum(lens)
-        ocu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(ospec.seed)
-        oq, ok_, ov = (torch.randn((oT, ospec.H, ospec.D), generator=gen, device=dev).to(torch.bfloat16)
-                       for _ in range(3))
-        oout = torch.empty_like(oq)
-        ows = torch.empty(vl.varlen_split_workspace_bytes(oT, len(lens), ospec.H, ospec.D), dtype=torch.uint8,
-                          device=dev)
-        ofn = lambda: vl.varlen_attn_fwd_split(oq, ok_, ov, ocu, ocu, max(lens), max(lens), wl.softmax_scale(ospec.D),
-                                               out=oout, workspace=ows)
-        for _ in range(3):
-            ofn()
-        oev = []
-        for _ in range(10):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            ofn()
-            b.record(stream)
-            oev.append((a, b))
-        torch.cuda.synchronize()
-        oms = float(np.median([a.elapsed_time(b) for a, b in oev]))
-        oflop = 4.0 * ospec.D * ospec.H * sum(x * x for x in lens)
-        otf = oflop / (oms * 1e-3) / 1e12
-        detail["attention_other_workloads"].append({
-            "workload": ospec.name, "total_tokens": oT, "requests": len(lens), "ms_median": round(oms, 4),
-            "TFLOP/s": round(otf, 2), "pct_of_bf16_peak": round(100 * otf / BF16_PEAK_TFLOPS, 2)})
-        err(f"[bench] attention at {other}: {oms:.3f} ms = {otf:.1f} TFLOP/s ({100 * otf / BF16_PEAK_TFLOPS:.1f}%)")
-        if other == "edit-cfg-4seq":
-            # the per-request CFG combine fused into the unpack of this output:
-            # sequences [r1+, r1-, r2+, r2-], image rows after each text piece,
-            # true CFG scale 4.0; reads two rows and writes one per output row
-            img = [int(h) * int(w) for h, w in ospec.img_grids]
-            ocu_h = np.concatenate([[0], np.cumsum(lens)])
-            nreq = len(lens) // 2
-            pos = torch.tensor([ocu_h[2 * r] + lens[2 * r] - img[2 * r] for r in range(nreq)], dtype=torch.int32,
+        # the per-request CFG combine fused into the unpack at the edit shape:
+        # sequences [r1+, r1-, r2+, r2-], image rows after each text piece,
+        # true CFG scale 4.0; reads two rows and writes one per output row
+        edit = next((s for s in steps_all if s.inp.spec.name == wl.WORKLOADS["edit-cfg-4seq"].name), None)
+        if edit is not None:
+            ei = edit.inp
+            cu_h = edit.cu_j.cpu().numpy()
+            nreq = ei.R // 2
+            img = ei.img_tokens
+            pos = torch.tensor([cu_h[2 * r] + ei.text_len[2 * r] for r in range(nreq)], dtype=torch.int32, device=dev)
+            neg = torch.tensor([cu_h[2 * r + 1] + ei.text_len[2 * r + 1] for r in range(nreq)], dtype=torch.int32,
                                device=dev)
-            neg = torch.tensor([ocu_h[2 * r + 1] + lens[2 * r + 1] - img[2 * r + 1] for r in range(nreq)],
-                               dtype=torch.int32, device=dev)
             seg = torch.tensor(np.concatenate([[0], np.cumsum(img[0::2])]), dtype=torch.int32, device=dev)
             cfg_s = torch.full((nreq,), 4.0, dtype=torch.float32, device=dev)
-            cdst = torch.empty((nreq, max(img[0::2]), ospec.H, ospec.D), dtype=torch.bfloat16, device=dev)
-            cfn = lambda: vl.unpack_cfg_combine(oout, seg, pos, neg, cfg_s, cdst)
-            for _ in range(3):
-                cfn()
-            cev = []
-            for _ in range(10):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                cfn()
-                b.record(stream)
-                cev.append((a, b))
-            torch.cuda.synchronize()
-            cus = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
-            cbytes = 3 * sum(img[0::2]) * ospec.H * ospec.D * 2
-            detail["cfg_combine_unpack"] = {"workload": ospec.name, "bytes": int(cbytes), "us_median": round(cus, 2),
-                                            "GB/s": round(cbytes / cus / 1e3, 1),
-                                            "pct_of_hbm": round(100 * cbytes / cus / 1e3 / HBM_PEAK_GBS, 1)}
-            err(f"[bench] CFG combine + unpack at {other}: {cus:.1f} us, "
-                f"{100 * cbytes / cus / 1e3 / HBM_PEAK_GBS:.1f}% of HBM")
+            cdst = torch.empty((nreq, max(img[0::2]), H, D), dtype=torch.bfloat16, device=dev)
+            cbytes = 3 * sum(img[0::2]) * ei.spec.H * ei.spec.D * 2
+            detail["cfg_combine_unpack"] = {"workload": ei.spec.name, **bw_record(
+                cbytes, lambda: vl.unpack_cfg_combine(edit.out, seg, pos, neg, cfg_s, cdst))}
+            err(f"[bench] CFG combine + unpack: warm {detail['cfg_combine_unpack']['warm']['pct_of_hbm']}% / "
+                f"flushed {detail['cfg_combine_unpack']['flushed']['pct_of_hbm']}% of HBM")
             del cdst
-        del oq, ok_, ov, oout, ows
+        for s in steps_all[1:]:
+            del s.packed, s.slabs, s.out, s.out_img, s.workspace
+        torch.cuda.empty_cache()
+
+        # block-local, one call per window type (cache flushed): % of MFMA
+        # peak as the metric asks, and % of HBM over its unique bytes (q, k, v
+        # read, out written) as the roofline
+        bl_bytes = 4 * bl_spec.B * bl_spec.n * bl_spec.H * bl_spec.D * 2
+        detail["block_local"] = []
+        win_us = {}
+        for (lb, la), o, npairs in zip(bl_spec.windows, bouts, bl_pairs):
+            med, p10, p90 = call_stats(
+                lambda: vl.block_local_attn_fwd(bq, bk, bv, bl_spec.block, lb, la, bl.scale, out=o), True)
+            fl = 4.0 * bl_spec.D * bl_spec.H * npairs
+            win_us[(lb, la)] = (med, fl)
+            detail["block_local"].append({"look_back": lb, "look_ahead": la, "us_median": round(med, 2),
+                                          "us_p10": round(p10, 2), "us_p90": round(p90, 2),
+                                          "TFLOP/s": round(fl / med / 1e6, 2),
+                                          "pct_of_bf16_peak": round(100 * fl / med / 1e6 / BF16_PEAK_TFLOPS, 3),
+                                          "pct_of_hbm_unique_bytes": round(100 * bl_bytes / med / 1e3 / HBM_PEAK_GBS,
+                                                                           1)})
+        err(f"[bench] block-local (flushed) us: {[d['us_median'] for d in detail['block_local']]}")
+        # the DiT's layer mix per forward: the configuration's 22 own-block
+        # layers + 3 layers with a block back and ahead, and the pages' 19
+        # own-block + 3 one-neighbour layers (one back / one ahead averaged)
+        own = win_us[(0, 0)]
+        one = ((win_us[(1, 0)][0] + win_us[(0, 1)][0]) / 2, (win_us[(1, 0)][1] + win_us[(0, 1)][1]) / 2)
+        both = win_us[(1, 1)]
+        detail["block_local_layer_mix"] = []
+        for name, mix in (("config 22 own-block + 3 both-neighbour layers", [(22, own), (3, both)]),
+                          ("pages 19 own-block + 3 one-neighbour layers", [(19, own), (3, one)])):
+            us = sum(c * t for c, (t, _) in mix)
+            fl = sum(c * f for c, (_, f) in mix)
+            detail["block_local_layer_mix"].append({"mix": name, "layers": sum(c for c, _ in mix),
+                                                    "us_per_forward": round(us, 2),
+                                                    "TFLOP/s": round(fl / us / 1e6, 2)})
+        # block-local at the DiT vocoder's production shape: CFG as batch 2,
+        # 4000 frames (167 blocks, the last of 16), own-block and one-neighbour
+        # windows, in the pages' fp32 and in bf16
+        prod_n, prod_b = 4000, 2
+        detail["block_local_production"] = []
+        for pdt in (torch.float32, torch.bfloat16):
+            pin = wl.make_block_local_inputs(bl_spec, pdt, n=prod_n, B=prod_b, seed=prod_n)
+            pq, pk, pv = pin.q.to(dev), pin.k.to(dev), pin.v.to(dev)
+            po = torch.empty_like(pq)
+            fn = vl.block_local_attn_fwd_f32 if pdt == torch.float32 else vl.block_local_attn_fwd
+            pbytes = 4 * prod_b * prod_n * bl_spec.H * bl_spec.D * pq.element_size()
+            for lb, la in ((0, 0), (1, 0), (0, 1)):
+                med, p10, p90 = call_stats(lambda: fn(pq, pk, pv, bl_spec.block, lb, la, pin.scale, out=po), True)
+                fl = 4.0 * bl_spec.D * bl_spec.H * prod_b * block_local_pairs(prod_n, bl_spec.block, lb, la)
+                detail["block_local_production"].append({
+                    "dtype": "f32" if pdt == torch.float32 else "bf16", "B": prod_b, "n": prod_n,
+                    "look_back": lb, "look_ahead": la, "us_median": round(med, 2), "us_p10": round(p10, 2),
+                    "us_p90": round(p90, 2), "TFLOP/s": round(fl / med / 1e6, 2),
+                    "pct_of_hbm_unique_bytes": round(100 * pbytes / med / 1e3 / HBM_PEAK_GBS, 1)})
+            del pq, pk, pv, po, pin
+        err(f"[bench] block-local production (flushed) us: "
+            f"{[(d['dtype'], d['look_back'], d['look_ahead'], d['us_median']) for d in detail['block_local_production']]}")
+        # launch floor on this stream: an event pair with nothing between, and
+        # one around a one-element kernel
+        one_el = torch.zeros(1, device=dev)
+        detail["launch_floor_us"] = {"empty_event_pair": round(call_stats(lambda: None, False)[0], 2),
+                                     "one_element_kernel": round(call_stats(lambda: one_el.add_(1.0), False)[0], 2)}
+        err(f"[bench] launch floor: {detail['launch_floor_us']}")
 
     cpu = None
-    if not args.no_cpu_baseline:
-        err("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(inp, cu_host)
-        err(f"[bench] oracle {cpu['value']} TFLOP/s on {cpu['cores']} threads")
+    if pool is not None:
+        err(f"[bench] timing the CPU oracle on a bounded sample ({workers} worker processes)")
+        cpu = run_cpu_baseline(pool, workers, share, args.cpu_budget)
+        err(f"[bench] oracle {cpu['value']} TFLOP/s; whole workload ~{cpu['full_workload_oracle_s_extrapolated']} s")
 
     line = {
         "metric": "varlen attention fwd TFLOP/s (in-request pairs) and % of bf16 MFMA peak",
@@ -424,9 +542,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic (seeded NumPy N(0,1) recipe at the pages' token shapes)",
         "config": {
-            "workload": workload,
+            "workload": f"{spec.name}+{bl_spec.name}-4windows",
             "total_tokens": T,
             "requests": R,
             "heads": H,
@@ -445,6 +563,7 @@ def main():
             "kernel": "vt_transpose_kernel<128> + attn_bf16_pp_kernel<128, 64, true> + "
                       "split_merge_kernel<128, 256> (varlen_attn_fwd_split)",
             "kernel_ms": round(attn_ms, 4),
+            "algorithmic_flop_per_launch": flop_varlen,
         },
         "cpu_baseline": cpu,
         "detail": detail,
