@@ -850,6 +850,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   st.init();
   f32x16 s[G::NKB];
   bf16x8 pf[G::NKC];
+#pragma unroll
+  for (int kc = 0; kc < G::NKC; ++kc) pf[kc] = bf16x8{};
   // Row sums of P on the matrix cores: a 16x16x32 MFMA reads the P^T operand
   // registers of the 32x32x16 PV step as its B operand (lane l: keys of its
   // lane group l/16, query n = l%16 of lanes l%32 < 16, n + 16 of the others)
@@ -875,54 +877,46 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
     return g == 0 ? (ql < 16 ? a0 : a1) : 0.f;
   };
 
-  // ---- MFMA phase of tile k: PV of tile k-1 (V in vl), then S of tile k (K in kl).
-  auto m_phase = [&](int k, const char* kl, const char* vl) {
-    if (k >= 1 && k <= ntiles) {
-      constexpr int VPF = 6;
-      constexpr int NSTEP = G::NKC * G::NDB;
-      auto read_v = [&](int step) {
+  // ---- MFMA phase of tile k: PV of tile k-1 (V in vl), then S of tile k (K
+  // in kl), as one stream of operand reads running PF steps ahead of the
+  // MFMAs, so the S part starts without waiting for its first reads.  Every
+  // phase runs both parts: in the first (k = 0) P is still zero (and the V
+  // buffer read was zeroed), after the last tile the scores are discarded.
+  auto m_phase = [&](const char* kl, const char* vl) {
+    constexpr int PF = 6;
+    constexpr int NV = G::NKC * G::NDB;
+    constexpr int NK = G::NKB * G::NDS;
+    auto read_op = [&](int i) {
+      if (i < NV) {
         if constexpr (kVt) {
-          return *(const bf16x8*)(vl + (((step % G::NDB) * 32 * VROW - kVtBias) + vt_rd[step / G::NDB]));
+          return *(const bf16x8*)(vl + (((i % G::NDB) * 32 * VROW - kVtBias) + vt_rd[i / G::NDB]));
         } else {
-          const char* p = vl + (step / G::NDB) * 16 * G::ROW + v_rd[step % G::NDB];
+          const char* p = vl + (i / G::NDB) * 16 * G::ROW + v_rd[i % G::NDB];
           const i16x4 lo4 = lds_read_tr(p);
           const i16x4 hi4 = lds_read_tr(p + 8 * G::ROW);
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         }
-      };
-      bf16x8 va[VPF + 1];
-#pragma unroll
-      for (int step = 0; step < VPF; ++step) va[step] = read_v(step);
-#pragma unroll
-      for (int step = 0; step < NSTEP; ++step) {
-        if (step + VPF < NSTEP) va[(step + VPF) % (VPF + 1)] = read_v(step + VPF);
-        VL_SCHED_BARRIER(0);
-        st.o[step % G::NDB] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[step / G::NDB], st.o[step % G::NDB], 0, 0, 0);
-        if (step % G::NDB == 0)
-          lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_sel, pf[step / G::NDB], lsum, 0, 0, 0);
-        VL_SCHED_BARRIER(0);
       }
-    }
-    if (k < ntiles) {
-      constexpr int KPF = 3;
-      constexpr int NSTEP = G::NKB * G::NDS;
-      auto read_k = [&](int step) {
-        return *(const bf16x8*)(kl + (step % G::NKB) * 32 * G::ROW + k_rd[step / G::NKB]);
-      };
+      const int ks = i - NV;  // key step of the S part
+      return *(const bf16x8*)(kl + (ks % G::NKB) * 32 * G::ROW + k_rd[ks / G::NKB]);
+    };
+    bf16x8 op[PF + 1];
 #pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb) s[kb] = f32x16{};
-      bf16x8 ka[KPF + 1];
+    for (int i = 0; i < PF; ++i) op[i] = read_op(i);
 #pragma unroll
-      for (int step = 0; step < KPF; ++step) ka[step] = read_k(step);
-#pragma unroll
-      for (int step = 0; step < NSTEP; ++step) {
-        if (step + KPF < NSTEP) ka[(step + KPF) % (KPF + 1)] = read_k(step + KPF);
-        VL_SCHED_BARRIER(0);
-        s[step % G::NKB] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[step / G::NKB], s[step % G::NKB], 0, 0, 0);
-        VL_SCHED_BARRIER(0);
+    for (int i = 0; i < NV + NK; ++i) {
+      if (i + PF < NV + NK) op[(i + PF) % (PF + 1)] = read_op(i + PF);
+      VL_SCHED_BARRIER(0);
+      if (i < NV) {
+        st.o[i % G::NDB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (PF + 1)], pf[i / G::NDB], st.o[i % G::NDB], 0, 0, 0);
+        if (i % G::NDB == 0) lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_sel, pf[i / G::NDB], lsum, 0, 0, 0);
+      } else {
+        const int ks = i - NV;
+        const f32x16 acc = ks < G::NKB ? f32x16{} : s[ks % G::NKB];
+        s[ks % G::NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (PF + 1)], qf[ks / G::NKB], acc, 0, 0, 0);
       }
+      VL_SCHED_BARRIER(0);
     }
   };
 
@@ -994,7 +988,8 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
     if constexpr (((I - GR) & 1) == 0) {
       // the MFMA wave wins issue arbitration on its SIMD during its phase
       __builtin_amdgcn_s_setprio(2);
-      if (wave_active) m_phase((p - GR) / 2, kbuf[(I / 2) % 3], vbuf[(I / 2 + 2) % 3]);
+      const int k = (p - GR) / 2;
+      if (wave_active && k <= ntiles) m_phase(kbuf[(I / 2) % 3], vbuf[(I / 2 + 2) % 3]);
       __builtin_amdgcn_s_setprio(0);
     } else {
       const char* src;
@@ -1048,8 +1043,11 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   copy_tile(kbase, false, 0, k0, ld_koff);
   copy_tile(kbase, false, 1, k1, ld_koff);
   copy_tile(vbase, kVt, 0, v0, ld_voff);
+  // the first MFMA phase of each group multiplies a zero P by buffer v2: it
+  // must hold finite values
+  for (int i = tid; i < G::kTileBytes / 16; i += 512) *(u32x4*)(v2 + 16 * i) = u32x4{};
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  wg_barrier();
+  __syncthreads();
   if (grp == 0)
     run(std::integral_constant<int, 0>{});
   else
