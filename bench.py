@@ -430,13 +430,52 @@ def main():
                 f"({detail['steps'][-1]['attention_pct_of_bf16_peak']}%)")
             steps_all.append(s)
 
+        def pipelined_flushed(fns, reps: int = 10):
+            """Per-call time of len(fns) calls on distinct buffers, queued back
+            to back after one flush (each call's data is cold: the others'
+            exceed the last-level cache); the launch gaps overlap the previous
+            call as in a pipeline.  Median over reps (us)."""
+            for f in fns:
+                f()
+            evs = []
+            for _ in range(reps):
+                torch.sum(flush)
+                a = new_event(stream)
+                for f in fns:
+                    f()
+                evs.append((a, new_event(stream)))
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) * 1e3 / len(fns) for a, b in evs]))
+
         detail["copies_alone"] = []
         for s in steps_all:
+            # two more buffer sets of the same copies for the pipelined figure
+            extra = []
+            for _ in range(2):
+                slabs = [(t.clone(), i.clone()) for t, i in s.slabs]
+                packed = [torch.empty_like(t) for t in s.packed]
+                pitems = []
+                for (txt, img), dst in zip(slabs, packed):
+                    pitems += [(txt, s.cu_t, dst, s.cu_j[:-1]), (img, s.cu_i, dst, s.img_dst)]
+                out = s.out.clone()
+                uitems = [(out, s.cu_t, torch.empty_like(s.out_txt), s.cu_j[:-1]),
+                          (out, s.cu_i, torch.empty_like(s.out_img), s.img_dst)]
+                extra.append((pitems, uitems))
             for what, fn, nbytes in (("pack", s.pack, s.pack_bytes), ("unpack", s.unpack, s.unpack_bytes)):
                 rec = {"workload": s.inp.spec.name, "copy": what, **bw_record(nbytes, fn)}
+                k = 0 if what == "pack" else 1
+                call = vl.pack_by_cu_seqlens_batched if what == "pack" else vl.unpack_by_cu_seqlens_batched
+                fns = [fn] + [(lambda it=e[k], c=call: c(it)) for e in extra]
+                us = pipelined_flushed(fns)
+                rec["pipelined_flushed"] = {"calls": len(fns), "us_per_call": round(us, 2),
+                                            "GB/s": round(nbytes / us / 1e3, 1),
+                                            "pct_of_hbm": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1)}
                 detail["copies_alone"].append(rec)
                 err(f"[bench] {what} at {s.inp.spec.name}: warm {rec['warm']['pct_of_hbm']}% / "
-                    f"flushed {rec['flushed']['pct_of_hbm']}% of HBM")
+                    f"flushed {rec['flushed']['pct_of_hbm']}% / pipelined flushed "
+                    f"{rec['pipelined_flushed']['pct_of_hbm']}% of HBM")
+            del extra
+            torch.cuda.empty_cache()
 
         # the per-request CFG combine fused into the unpack at the edit shape:
         # sequences [r1+, r1-, r2+, r2-], image rows after each text piece,

@@ -213,6 +213,9 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[NKB], int key0, int g, i
 
 // s_waitcnt immediate (gfx9 encoding) that waits for all vector-memory operations.
 constexpr int kWaitVm0 = 0x0F70;
+// ... and one that waits until at most n (< 64) of them are outstanding
+// (vmcnt bits 3:0 and 15:14).
+constexpr int wait_vm(int n) { return kWaitVm0 | (n & 15) | ((n >> 4) << 14); }
 // Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
 [[maybe_unused]] constexpr int kBufferFlags = 0x00020000;  // (used in the device pass only)
 
@@ -1254,101 +1257,153 @@ __global__ void __launch_bounds__(256, 2) attn_f32_kernel(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- block-local fp32, block-aligned
+// ---------------------------------------------------------------- block-local, block-aligned (D = 64)
 
-// Block-local attention in fp32 with the work cut along the blocks: every
-// query of block b sees the same keys (the frames of blocks
-// [b - look_back, b + look_ahead] that exist), so one wave takes one query
-// block of one (batch, head) -- up to 32 rows, the MFMA tile's width -- and
-// only its window's keys, in chunks of 32.  No LDS and no barrier: K is read
-// straight into the A operand registers, V element by element (the lanes of
-// a half read one 128-byte row segment).  Against tiles of 128 rows over the
-// union of their rows' windows this cuts the fp32 MFMA work 2-4.5x at the
-// Token2Wav shape (24-frame blocks).
+// Every query of block b sees the same keys, so for blocks of <= 32 frames one
+// wave takes one query block of one (batch, head) and exactly its window, in
+// chunks of 32 keys: no LDS sharing, no barriers, no masking beyond the
+// window's ragged end.  Addressing: the wave's unit decides a uniform base
+// pointer per tensor (its batch row and head, its first query / window key),
+// lanes add 32-bit row offsets (24-bit multiplies), and buffer descriptors
+// spanning only the valid rows make reads past the block or the window
+// return zeros (those scores are masked, those query rows never stored).
+struct BlockUnit {
+  int b, h, r0, nq, k_lo, k_hi;
+};
+
+// Grid (ceil(nb / 4), H, B): wave w of work-group x takes query block 4x + w
+// (neighbouring blocks, which share keys, in neighbouring waves) of head y
+// and batch row z.
+__device__ __forceinline__ BlockUnit block_unit(const AttnArgs& a, int qb, int nb) {
+  BlockUnit u;
+  u.h = blockIdx.y;
+  u.b = blockIdx.z;
+  u.r0 = qb * a.block;
+  u.nq = min(a.block, a.n - u.r0);
+  u.k_lo = max(0, qb - a.look_back) * a.block;
+  u.k_hi = min((qb + min(a.look_ahead, nb - 1 - qb)) * a.block + a.block, a.n);
+  return u;
+}
+
+// Buffer resource over `rows` rows of `rs` bytes (the last one `row_bytes`
+// long) from `base`; reads past them return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int rs, int row_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows > 0 ? (rows - 1) * rs + row_bytes : 0, kBufferFlags);
+}
+
+// fp32 (the Token2Wav DiT's precision):
 //   S^T = K Q^T with v_mfma_f32_32x32x2_f32: lane (ql, g) holds the 16-byte
 //   chunks 2i + g (features 8i + 4g .. +3, i = 0..7) of query row ql (B
 //   operand) and of key row ql of the chunk (A operand), so the two halves of
 //   a load read the same 128-byte lines; step 4i + e contracts feature
-//   8i + 4g + e of both halves.  The
-//   result gives lane (ql, g) the scores of query ql for keys score_key(0, j, g).
+//   8i + 4g + e of both halves.  Two accumulators (even and odd steps) halve
+//   the dependent chain.  The result gives lane (ql, g) the scores of query
+//   ql for keys score_key(0, j, g).
 //   O^T += V^T P^T: step j contracts key score_key(0, j, g) of each half, whose
-//   probability is the lane's own score register j (see the tiled kernel).
+//   probability is the lane's own score register j.  The chunk's V rows are
+//   copied straight to LDS (256-byte rows; rows 4..7 of each group of 8 have
+//   their two 128-byte halves swapped, so the two lane halves of a read --
+//   rows 4 apart -- hit different banks) and each operand is one 4-byte read.
+// One LDS buffer per wave (32 KB per work-group): the next chunk's V copy
+// starts after this chunk's PV reads, and three waves fit on each SIMD (162
+// VGPRs); double-buffering V (64 KB per work-group, two waves per SIMD) was
+// slower at every window.
 template <int D>
-__global__ void __launch_bounds__(256) block_local_f32_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, 3) block_local_f32_kernel(AttnArgs a) {
   static_assert(D == 64, "two lane halves of 32 features");
   constexpr int NQ = D / 2;
   constexpr int NDB = D / 32;
+  constexpr int VCH = 32 * D * 4;  // bytes of one chunk of V in LDS
+  __shared__ __attribute__((aligned(16))) char vlds[4][VCH];
   const int lane = threadIdx.x & 63;
   const int ql = lane & 31;
   const int g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = (a.n + a.block - 1) / a.block;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= (int64_t)a.B * a.H * nb) return;
-  const int qb = (int)(unit % nb);  // neighbouring blocks (shared keys) in neighbouring waves
-  const int h = (int)((unit / nb) % a.H);
-  const int b = (int)(unit / ((int64_t)nb * a.H));
-  const int H = a.H;
-  const int64_t row_stride = (int64_t)H * D;
-  const int64_t base = (int64_t)b * a.n * row_stride + (int64_t)h * D;
+  const int qb = blockIdx.x * 4 + wave;
+  if (qb >= nb) return;
+  const BlockUnit u = block_unit(a, qb, nb);
+  const int rs = a.H * D * 4;  // bytes between consecutive frames
+  const int64_t hoff = (int64_t)u.b * a.n * a.H * D + (int64_t)u.h * D;
+  const float* qb_ = (const float*)a.q + hoff + (int64_t)u.r0 * a.H * D;
+  const float* kb_ = (const float*)a.k + hoff + (int64_t)u.k_lo * a.H * D;
+  const float* vb_ = (const float*)a.v + hoff + (int64_t)u.k_lo * a.H * D;
+  const int nkeys = u.k_hi - u.k_lo;
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qb_, u.nq, rs, D * 4);
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb_, nkeys, rs, D * 4);
 
-  const int r0 = qb * a.block;
-  const int nq = min(a.block, a.n - r0);
-  const int k_lo = max(0, qb - a.look_back) * a.block;
-  const int k_hi = min((qb + min(a.look_ahead, nb - 1 - qb)) * a.block + a.block, a.n);
-
-  const float* __restrict__ qg = (const float*)a.q;
-  const float* __restrict__ kg = (const float*)a.k;
-  const float* __restrict__ vg = (const float*)a.v;
-
-  // query rows past the block's end repeat its last row (computed, not stored)
+  // lane (ql, g): row ql, 16-byte chunks 2i + g
+  const uint32_t lrow = (uint32_t)__umul24(ql, rs) + 16 * g;
   float qf[NQ];
-  {
-    const float* qp = qg + base + (int64_t)(r0 + min(ql, nq - 1)) * row_stride + 4 * g;
 #pragma unroll
-    for (int s4 = 0; s4 < NQ / 4; ++s4) {
-      const f32x4 x = *(const f32x4*)(qp + 8 * s4);
+  for (int i = 0; i < NQ / 4; ++i) {
+    const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, lrow + 32 * i, 0, 0));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[4 * s4 + e] = x[e];
-    }
+    for (int e = 0; e < 4; ++e) qf[4 * i + e] = x[e];
   }
+  // V copy: lane l of load i fills LDS row 4i + l/16, physical chunk l%16,
+  // from logical chunk (l%16) ^ 8(i&1)
+  auto copy_v = [&](int c, char* dst) {
+    const char* src = (const char*)vb_ + (int64_t)c * 32 * rs;
+    const int rows = min(32, nkeys - c * 32);
+#pragma unroll
+    for (int i = 0; i < VCH / 1024; ++i) {
+      const int row = 4 * i + lane / 16;
+      const uint32_t voff = (uint32_t)__umul24(row, rs) + (((lane & 15) ^ (8 * (i & 1))) * 16);
+      lds_dma_one(src, (rows - 1) * rs + D * 4, dst + i * 1024, voff);
+    }
+  };
+  auto load_k = [&](int c, float (&kf)[NQ]) {
+#pragma unroll
+    for (int i = 0; i < NQ / 4; ++i) {
+      const f32x4 x = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lrow + (uint32_t)(c * 32) * rs + 32 * i, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kf[4 * i + e] = x[e];
+    }
+  };
+  // PV operand reads: key score_key(0, j, g), feature db*32 + ql, at
+  // row*256 + (db ^ g)*128 + 4 ql
+  const int vrd0 = 4 * g * 256 + g * 128 + 4 * ql;
+  const int vrd1 = 4 * g * 256 + (1 - g) * 128 + 4 * ql;
 
   RowState<1, NDB> st;
   st.init();
-  for (int key0 = k_lo; key0 < k_hi; key0 += 32) {
-    // keys past the window's end read its last row (finite; masked below)
-    float kf[NQ];
-    {
-      const float* kp = kg + base + (int64_t)min(key0 + ql, k_hi - 1) * row_stride + 4 * g;
+  const int nch = (nkeys + 31) / 32;
+  float kf[NQ];
+  load_k(0, kf);
+  char* const vbuf = vlds[wave];
+  copy_v(0, vbuf);
+  for (int c = 0; c < nch; ++c) {
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-      for (int s4 = 0; s4 < NQ / 4; ++s4) {
-        const f32x4 x = *(const f32x4*)(kp + 8 * s4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kf[4 * s4 + e] = x[e];
-      }
+    for (int st4 = 0; st4 < NQ; st4 += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[st4], qf[st4], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[st4 + 1], qf[st4 + 1], s1, 0, 0, 0);
     }
-    float vf[16][NDB];
+    f32x16 s[1] = {s0 + s1};
+    const int key0 = u.k_lo + c * 32;
+    // the next chunk's K rows stream in while this one computes
+    if (c + 1 < nch) load_k(c + 1, kf);
+    if (key0 + 32 > u.k_hi) mask_scores<1>(s, key0, g, u.k_lo, u.k_hi);
+    st.softmax_tile(s, a.c);
+    // this chunk's V copy has landed
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float* vp = vg + base + (int64_t)min(key0 + score_key(0, j, g), k_hi - 1) * row_stride + ql;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) vf[j][db] = vp[db * 32];
+      const int rowoff = (8 * (j >> 2) + (j & 3)) * 256;
+      const float v0 = *(const float*)(vbuf + rowoff + vrd0);
+      const float v1 = *(const float*)(vbuf + rowoff + vrd1);
+      st.o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, s[0][j], st.o[0], 0, 0, 0);
+      st.o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, s[0][j], st.o[1], 0, 0, 0);
     }
-    f32x16 s[1] = {f32x16{}};
-#pragma unroll
-    for (int st4 = 0; st4 < NQ; ++st4) s[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[st4], qf[st4], s[0], 0, 0, 0);
-    if (key0 + 32 > k_hi) mask_scores<1>(s, key0, g, k_lo, k_hi);
-    st.softmax_tile(s, a.c);
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[j][db], s[0][j], st.o[db], 0, 0, 0);
+    if (c + 1 < nch) copy_v(c + 1, vbuf);
   }
 
   const float l_tot = pair_sum(st.l);
-  if (ql < nq) {
-    const int64_t row = base + (int64_t)(r0 + ql) * row_stride;
-    float* op = (float*)a.out + row;
+  if (ql < u.nq) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    float* op = (float*)a.out + hoff + (int64_t)(u.r0 + ql) * a.H * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1356,115 +1411,133 @@ __global__ void __launch_bounds__(256) block_local_f32_kernel(AttnArgs a) {
         const int d = db * 32 + 8 * i + 4 * g;
         f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = l_tot > 0.f ? st.o[db][4 * i + e] / l_tot : 0.f;
+        for (int e = 0; e < 4; ++e) w[e] = st.o[db][4 * i + e] * inv;
         *(f32x4*)(op + d) = w;
       }
     if (a.lse != nullptr && g == 0)
-      a.lse[((int64_t)b * a.n + r0 + ql) * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[((int64_t)u.b * a.n + u.r0 + ql) * a.H + u.h] =
+          l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
-// ---------------------------------------------------------------- block-local bf16, block-aligned
-
-// The bf16 counterpart of block_local_f32_kernel (D = 64, blocks of <= 32
-// frames): one wave per query block of one (batch, head), its window's keys
-// in chunks of 32, no LDS, no barriers.  Operands as in the varlen kernel:
+// bf16, same scheme:
 //   S^T = K Q^T (v_mfma_f32_32x32x16_bf16, 4 steps over D): lane (ql, g)
 //   holds features 16 ds + 8g .. +7 of query row ql (B) and of key row ql of
 //   the chunk (A), one 16-byte load each.
 //   O^T += V^T P^T (2 key steps x 2 feature blocks): P^T(kc) is the lane's
 //   score registers 8kc .. 8kc+7 rounded to bf16, i.e. keys
-//   16kc + 4g + (i & 3) + 8(i >> 2), i = 0..7; the V^T operand of lane (ql, g)
-//   holds feature 32 db + ql of those same keys, gathered element by element
-//   (a lane half reads 64 contiguous bytes of one key row per element).
-template <int D>
-__global__ void __launch_bounds__(256) block_local_bf16_kernel(AttnArgs a) {
+//   16kc + 4g + (i & 3) + 8(i >> 2), i = 0..7; the chunk's V rows are copied
+//   straight to LDS (128-byte rows, 16-byte chunks XOR-swizzled by row) and
+//   the V^T operands read back with two transposing reads each
+//   (ds_read_b64_tr_b16), which deliver exactly those keys of one feature.
+// NBUF = 2 for windows of two chunks: the next chunk's V streams into the
+// other LDS buffer while this one computes; 1 for single-chunk windows.
+template <int D, int NBUF>
+__global__ void __launch_bounds__(256, 3) block_local_bf16_kernel(AttnArgs a) {
   static_assert(D == 64, "four 16-feature MFMA steps");
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int ROW = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int VCH = 32 * ROW;
+  __shared__ __attribute__((aligned(16))) char vlds[4][NBUF][VCH];
   const int lane = threadIdx.x & 63;
   const int ql = lane & 31;
   const int g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = (a.n + a.block - 1) / a.block;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= (int64_t)a.B * a.H * nb) return;
-  const int qb = (int)(unit % nb);  // neighbouring blocks (shared keys) in neighbouring waves
-  const int h = (int)((unit / nb) % a.H);
-  const int b = (int)(unit / ((int64_t)nb * a.H));
-  const int H = a.H;
-  const int64_t row_stride = (int64_t)H * D;
-  const int64_t base = (int64_t)b * a.n * row_stride + (int64_t)h * D;
+  const int qb = blockIdx.x * 4 + wave;
+  if (qb >= nb) return;
+  const BlockUnit u = block_unit(a, qb, nb);
+  const int rs = a.H * D * 2;
+  const int64_t hoff = (int64_t)u.b * a.n * a.H * D + (int64_t)u.h * D;
+  const __bf16* qb_ = (const __bf16*)a.q + hoff + (int64_t)u.r0 * a.H * D;
+  const __bf16* kb_ = (const __bf16*)a.k + hoff + (int64_t)u.k_lo * a.H * D;
+  const __bf16* vb_ = (const __bf16*)a.v + hoff + (int64_t)u.k_lo * a.H * D;
+  const int nkeys = u.k_hi - u.k_lo;
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qb_, u.nq, rs, ROW);
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kb_, nkeys, rs, ROW);
 
-  const int r0 = qb * a.block;
-  const int nq = min(a.block, a.n - r0);
-  const int k_lo = max(0, qb - a.look_back) * a.block;
-  const int k_hi = min((qb + min(a.look_ahead, nb - 1 - qb)) * a.block + a.block, a.n);
-
-  const __bf16* __restrict__ qg = (const __bf16*)a.q;
-  const __bf16* __restrict__ kg = (const __bf16*)a.k;
-  const __bf16* __restrict__ vg = (const __bf16*)a.v;
-
-  // query rows past the block's end repeat its last row (computed, not stored)
+  const uint32_t lrow = (uint32_t)__umul24(ql, rs) + 16 * g;
   bf16x8 qf[NDS];
-  {
-    const __bf16* qp = qg + base + (int64_t)(r0 + min(ql, nq - 1)) * row_stride + 8 * g;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qf[ds] = *(const bf16x8*)(qp + 16 * ds);
+  for (int ds = 0; ds < NDS; ++ds)
+    qf[ds] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, lrow + 32 * ds, 0, 0));
+  // V copy: lane l of load i fills LDS row 8i + l/8, physical chunk l%8, from
+  // logical chunk (l%8) ^ v_swz(row)
+  auto copy_v = [&](int c, char* dst) {
+    const char* src = (const char*)vb_ + (int64_t)c * 32 * rs;
+    const int rows = min(32, nkeys - c * 32);
+#pragma unroll
+    for (int i = 0; i < VCH / 1024; ++i) {
+      const int row = 8 * i + lane / CPR;
+      const uint32_t voff = (uint32_t)__umul24(row, rs) + (((lane % CPR) ^ v_swz<CPR>(row)) * 16);
+      lds_dma_one(src, (rows - 1) * rs + ROW, dst + i * 1024, voff);
+    }
+  };
+  auto load_k = [&](int c, bf16x8 (&kf)[NDS]) {
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+      kf[ds] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lrow + (uint32_t)(c * 32) * rs + 32 * ds, 0, 0));
+  };
+  // transposing-read offsets: in 16-lane group G' (lane half g = G'/2,
+  // feature half G' % 2) input lane i points at row 4g + i/4 (and + 8) of a
+  // 16-key step, features db*32 + 16*(G' % 2) + 4*(i % 4) .. +3
+  const int vgrp = lane >> 4;
+  const int gi = lane & 15;
+  const int v_row = 4 * (vgrp >> 1) + (gi >> 2);
+  int v_rd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int byte_in_row = db * 64 + 32 * (vgrp & 1) + 8 * (gi & 3);
+    v_rd[db] = v_row * ROW + (((byte_in_row >> 4) ^ v_swz<CPR>(v_row)) * 16) + (byte_in_row & 15);
   }
 
   RowState<1, NDB> st;
   st.init();
-  // keys past the window's end read its last row (finite; masked below)
-  auto load_chunk = [&](int key0, bf16x8 (&kf)[NDS], bf16x8 (&vt)[2][NDB]) {
-    const __bf16* kp = kg + base + (int64_t)min(key0 + ql, k_hi - 1) * row_stride + 8 * g;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) kf[ds] = *(const bf16x8*)(kp + 16 * ds);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = min(key0 + 16 * kc + 4 * g + (i & 3) + 8 * (i >> 2), k_hi - 1);
-        const __bf16* vp = vg + base + (int64_t)key * row_stride + ql;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vt[kc][db][i] = vp[32 * db];
-      }
-  };
-  auto compute_chunk = [&](int key0, const bf16x8 (&kf)[NDS], const bf16x8 (&vt)[2][NDB]) {
+  const int nch = (nkeys + 31) / 32;
+  bf16x8 kf[NDS];
+  load_k(0, kf);
+  copy_v(0, vlds[wave][0]);
+  for (int c = 0; c < nch; ++c) {
+    char* vbuf = vlds[wave][NBUF > 1 ? (c & 1) : 0];
     f32x16 s[1] = {f32x16{}};
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds], qf[ds], s[0], 0, 0, 0);
-    if (key0 + 32 > k_hi) mask_scores<1>(s, key0, g, k_lo, k_hi);
+    const int key0 = u.k_lo + c * 32;
+    if (c + 1 < nch) {
+      load_k(c + 1, kf);
+      if (NBUF > 1) copy_v(c + 1, vlds[wave][(c + 1) & 1]);
+    }
+    if (key0 + 32 > u.k_hi) mask_scores<1>(s, key0, g, u.k_lo, u.k_hi);
     st.softmax_tile(s, a.c);
     bf16x8 pf[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)s[0][8 * kc + e];
+    if (NBUF > 1 && c + 1 < nch)
+      __builtin_amdgcn_s_waitcnt(wait_vm(NDS + VCH / 1024));  // only the next chunk's loads outstanding
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[kc][db], pf[kc], st.o[db], 0, 0, 0);
-  };
-  // chunk c + 1 is loaded while chunk c is computed (two register sets)
-  bf16x8 kfa[NDS], vta[2][NDB], kfb[NDS], vtb[2][NDB];
-  load_chunk(k_lo, kfa, vta);  // the window is never empty
-  for (int key0 = k_lo;;) {
-    const int k1 = key0 + 32;
-    if (k1 < k_hi) load_chunk(k1, kfb, vtb);
-    compute_chunk(key0, kfa, vta);
-    if (k1 >= k_hi) break;
-    const int k2 = k1 + 32;
-    if (k2 < k_hi) load_chunk(k2, kfa, vta);
-    compute_chunk(k1, kfb, vtb);
-    if (k2 >= k_hi) break;
-    key0 = k2;
+      for (int db = 0; db < NDB; ++db) {
+        const char* p = vbuf + kc * 16 * ROW + v_rd[db];
+        const i16x4 lo4 = lds_read_tr(p);
+        const i16x4 hi4 = lds_read_tr(p + 8 * ROW);
+        const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf[kc], st.o[db], 0, 0, 0);
+      }
+    if (NBUF == 1 && c + 1 < nch) copy_v(c + 1, vbuf);
   }
 
   const float l_tot = pair_sum(st.l);
-  if (ql < nq) {
+  if (ql < u.nq) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    __bf16* op = (__bf16*)a.out + base + (int64_t)(r0 + ql) * row_stride;
+    __bf16* op = (__bf16*)a.out + hoff + (int64_t)(u.r0 + ql) * a.H * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1477,7 +1550,8 @@ __global__ void __launch_bounds__(256) block_local_bf16_kernel(AttnArgs a) {
         *(bf16x4*)(op + d) = w;
       }
     if (a.lse != nullptr && g == 0)
-      a.lse[((int64_t)b * a.n + r0 + ql) * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[((int64_t)u.b * a.n + u.r0 + ql) * a.H + u.h] =
+          l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -1851,23 +1925,27 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
   a.look_ahead = min(look_ahead, nblocks);
   a.nqt = nqt;
   (void)hipGetLastError();
-  if (kF32 && D == 64 && block <= 32) {
-    // one wave per query block of one (batch, head)
-    const int64_t units = (int64_t)B * H * ((n + block - 1) / block);
-    if ((units + 3) / 4 > INT32_MAX) return VL_EUNSUPPORTED;
-    hipLaunchKernelGGL((vl::block_local_f32_kernel<64>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+  // one wave per query block of one (batch, head), its window in 32-key
+  // chunks (D = 64, blocks of <= 32 frames); its 32-bit row offsets need the
+  // sequence's rows within 2^31 bytes
+  const int64_t window = (int64_t)(1 + a.look_back + a.look_ahead) * block;
+  const bool aligned = D == 64 && block <= 32 && (int64_t)n * H * D * (kF32 ? 4 : 2) < INT32_MAX && H <= 65535 &&
+                       B <= 65535;
+  const bool one_chunk = window <= 32;
+  const int64_t nblk = (n + block - 1) / block;
+  const dim3 ag((unsigned)((nblk + 3) / 4), (unsigned)H, (unsigned)B);
+  if (kF32 && aligned) {
+    hipLaunchKernelGGL((vl::block_local_f32_kernel<64>), ag, dim3(256), 0, stream, a);
   } else if (kF32) {
     if (D == 128)
       hipLaunchKernelGGL((vl::attn_f32_kernel<128, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
-  } else if (D == 64 && block <= 32 && (int64_t)(1 + a.look_back + a.look_ahead) * block <= 64) {
-    // windows of up to two 32-key chunks (own block, one neighbour at blocks
-    // of 24): one wave per query block; wider windows go to the tiled kernel,
-    // whose pipelined tiles hide their loads better
-    const int64_t units = (int64_t)B * H * ((n + block - 1) / block);
-    if ((units + 3) / 4 > INT32_MAX) return VL_EUNSUPPORTED;
-    hipLaunchKernelGGL((vl::block_local_bf16_kernel<64>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+  } else if (aligned && window <= 64) {
+    if (one_chunk)
+      hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 1>), ag, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 2>), ag, dim3(256), 0, stream, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL((vl::attn_bf16_kernel<128, 4, 1, 64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
