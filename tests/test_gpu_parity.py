@@ -655,6 +655,36 @@ def test_block_local_other_shapes(case, f32):
     check_lse(to64(lse), rl, f32, f"block-local {case}", rounded_weights=False)
 
 
+# Random small shapes through the block-aligned kernels (D = 64, blocks of
+# 1..32 frames: one wave per query block, buffer loads bounded to the valid
+# rows, V through LDS) and the tiled fallbacks (blocks above 32, wider bf16
+# windows): batch rows, head counts, ragged last blocks and windows that
+# reach past either end, each with canary rows around out and lse.
+_BL_RNG = np.random.default_rng(77)
+BL_RANDOM = [tuple(int(_BL_RNG.integers(lo, hi)) for lo, hi in ((1, 4), (1, 260), (1, 5), (1, 41), (0, 4), (0, 4)))
+             for _ in range(12)]
+
+
+@pytest.mark.parametrize("case", BL_RANDOM)
+@pytest.mark.parametrize("f32", [False, True])
+def test_block_local_random_shapes(case, f32):
+    B, n, H, block, lb, la = case
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[block_local] random B={B} n={n} H={H} block={block} lb={lb} la={la} {dtype}")
+    rng = np.random.default_rng(n * 131 + block)
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, n, H, 64)).astype(np.float32)).to(dtype) for _ in range(3))
+    fn = vl.block_local_attn_fwd_f32 if f32 else vl.block_local_attn_fwd
+    full, out = canary_out(tuple(q.shape), dtype, pad=1)
+    lse_full, lse = canary_out((B, n, H), torch.float32, pad=1)
+    fn(q.to(DEV), k.to(DEV), v.to(DEV), block, lb, la, 0.125, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert_canary(full, pad=1)
+    assert_canary(lse_full, pad=1)
+    ro, rl = oracle.block_local_attention(to64(q), to64(k), to64(v), block, lb, la, 0.125)
+    check_close(to64(out), ro, f32, f"block-local random {case}")
+    check_lse(to64(lse), rl, f32, f"block-local random {case}", rounded_weights=False)
+
+
 @pytest.mark.parametrize("f32", [False, True])
 def test_block_local_own_block_agrees_with_varlen_on_block_requests(f32):
     """Own-block windows with n a multiple of the block are varlen attention
