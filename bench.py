@@ -22,7 +22,8 @@ block-local pairs); work the kernels avoid is never counted.
 
 The `detail` object holds the same step at the two other full-size workloads,
 the bandwidth-bound pieces alone (warm and with the last-level cache flushed),
-the block-local calls per window and weighted by the DiT's layer mix, the
+each beside the runtime's own device-to-device memcpy of the same bytes timed
+the same way (the practical ceiling at that size), the block-local calls per window and weighted by the DiT's layer mix, the
 production block-local shape, the fused CFG combine, and the launch floor.
 The CPU baseline is the fp64 oracle run by a process pool (one BLAS thread per
 worker) on a bounded sample of the headline workload's (request, head, query
@@ -447,6 +448,26 @@ def main():
             torch.cuda.synchronize()
             return float(np.median([a.elapsed_time(b) * 1e3 / len(fns) for a, b in evs]))
 
+        def memcpy_reference(nbytes, pipelined: bool = True):
+            """The runtime's own device-to-device copy (hipMemcpyAsync through
+            torch's copy_) moving the same bytes (half read, half written),
+            timed the same ways: the practical ceiling for a copy of this size."""
+            n = int(nbytes) // 4 * 2
+            bufs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(1), torch.empty(n, dtype=torch.uint8,
+                                                                                        device=dev))
+                    for _ in range(3 if pipelined else 1)]
+            fns = [(lambda a=a, b=b: b.copy_(a)) for a, b in bufs]
+            rec = {}
+            for tag, fl in (("warm", False), ("flushed", True)):
+                med = call_stats(fns[0], fl)[0]
+                rec[tag] = {"us_median": round(med, 2), "pct_of_hbm": round(100 * 2 * n / med / 1e3 / HBM_PEAK_GBS, 1)}
+            if pipelined:
+                us = pipelined_flushed(fns)
+                rec["pipelined_flushed"] = {"us_per_call": round(us, 2),
+                                            "pct_of_hbm": round(100 * 2 * n / us / 1e3 / HBM_PEAK_GBS, 1)}
+            del bufs, fns
+            return rec
+
         detail["copies_alone"] = []
         for s in steps_all:
             # two more buffer sets of the same copies for the pipelined figure
@@ -470,10 +491,14 @@ def main():
                 rec["pipelined_flushed"] = {"calls": len(fns), "us_per_call": round(us, 2),
                                             "GB/s": round(nbytes / us / 1e3, 1),
                                             "pct_of_hbm": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1)}
+                rec["memcpy_same_bytes"] = memcpy_reference(nbytes)
                 detail["copies_alone"].append(rec)
+                m = rec["memcpy_same_bytes"]
                 err(f"[bench] {what} at {s.inp.spec.name}: warm {rec['warm']['pct_of_hbm']}% / "
                     f"flushed {rec['flushed']['pct_of_hbm']}% / pipelined flushed "
-                    f"{rec['pipelined_flushed']['pct_of_hbm']}% of HBM")
+                    f"{rec['pipelined_flushed']['pct_of_hbm']}% of HBM (memcpy of the same bytes: "
+                    f"{m['warm']['pct_of_hbm']} / {m['flushed']['pct_of_hbm']} / "
+                    f"{m['pipelined_flushed']['pct_of_hbm']}%)")
             del extra
             torch.cuda.empty_cache()
 
@@ -494,7 +519,8 @@ def main():
             cdst = torch.empty((nreq, max(img[0::2]), H, D), dtype=torch.bfloat16, device=dev)
             cbytes = 3 * sum(img[0::2]) * ei.spec.H * ei.spec.D * 2
             detail["cfg_combine_unpack"] = {"workload": ei.spec.name, **bw_record(
-                cbytes, lambda: vl.unpack_cfg_combine(edit.out, seg, pos, neg, cfg_s, cdst))}
+                cbytes, lambda: vl.unpack_cfg_combine(edit.out, seg, pos, neg, cfg_s, cdst)),
+                "memcpy_same_bytes": memcpy_reference(cbytes, pipelined=False)}
             err(f"[bench] CFG combine + unpack: warm {detail['cfg_combine_unpack']['warm']['pct_of_hbm']}% / "
                 f"flushed {detail['cfg_combine_unpack']['flushed']['pct_of_hbm']}% of HBM")
             del cdst
@@ -519,7 +545,9 @@ def main():
                                           "pct_of_bf16_peak": round(100 * fl / med / 1e6 / BF16_PEAK_TFLOPS, 3),
                                           "pct_of_hbm_unique_bytes": round(100 * bl_bytes / med / 1e3 / HBM_PEAK_GBS,
                                                                            1)})
-        err(f"[bench] block-local (flushed) us: {[d['us_median'] for d in detail['block_local']]}")
+        detail["block_local_memcpy_same_bytes"] = memcpy_reference(bl_bytes, pipelined=False)
+        err(f"[bench] block-local (flushed) us: {[d['us_median'] for d in detail['block_local']]} "
+            f"(memcpy of the same bytes, flushed: {detail['block_local_memcpy_same_bytes']['flushed']['us_median']})")
         # the DiT's layer mix per forward: the configuration's 22 own-block
         # layers + 3 layers with a block back and ahead, and the pages' 19
         # own-block + 3 one-neighbour layers (one back / one ahead averaged)
@@ -534,6 +562,38 @@ def main():
             detail["block_local_layer_mix"].append({"mix": name, "layers": sum(c for c, _ in mix),
                                                     "us_per_forward": round(us, 2),
                                                     "TFLOP/s": round(fl / us / 1e6, 2)})
+        # the same mixes as a forward issues them: every layer's call queued
+        # back to back on its own q/k/v/out (each layer has its own
+        # activations) after one flush, so launch gaps overlap the previous
+        # call; the windowed layers spread evenly over the stack.  The pages'
+        # one-neighbour layers: all one back, then all one ahead, averaged.
+        n_layers = 25
+        lay = [tuple(t.clone() for t in (bq, bk, bv)) + (torch.empty_like(bq),) for _ in range(n_layers)]
+
+        def forward_us(windows, reps: int = 10):
+            calls = [(lambda x=lay[i], w=windows[i]: vl.block_local_attn_fwd(
+                x[0], x[1], x[2], bl_spec.block, w[0], w[1], bl.scale, out=x[3])) for i in range(len(windows))]
+            return pipelined_flushed(calls, reps) * len(calls)
+
+        def spread(n, special, w_special):
+            pos = {round((j + 1) * n / (len(special) + 1)) - 1 for j in range(len(special))}
+            it = iter(w_special)
+            return [next(it) if i in pos else (0, 0) for i in range(n)]
+
+        fl_of = {w: f for w, (_, f) in win_us.items()}
+        detail["block_local_layer_mix_pipelined"] = []
+        for name, variants in (
+                ("config 22 own-block + 3 both-neighbour layers", [spread(25, [0] * 3, [(1, 1)] * 3)]),
+                ("pages 19 own-block + 3 one-neighbour layers", [spread(22, [0] * 3, [(1, 0)] * 3),
+                                                                 spread(22, [0] * 3, [(0, 1)] * 3)])):
+            us = float(np.mean([forward_us(v) for v in variants]))
+            fl = float(np.mean([sum(fl_of[w] for w in v) for v in variants]))
+            detail["block_local_layer_mix_pipelined"].append({
+                "mix": name, "layers": len(variants[0]), "us_per_forward": round(us, 2),
+                "us_per_layer": round(us / len(variants[0]), 2), "TFLOP/s": round(fl / us / 1e6, 2)})
+        err(f"[bench] block-local layer mix, queued as a forward: "
+            f"{[(d['layers'], d['us_per_forward'], d['us_per_layer']) for d in detail['block_local_layer_mix_pipelined']]}")
+        del lay
         # block-local at the DiT vocoder's production shape: CFG as batch 2,
         # 4000 frames (167 blocks, the last of 16), own-block and one-neighbour
         # windows, in the pages' fp32 and in bf16

@@ -85,11 +85,13 @@ struct CopyBatch {
 
 template <bool kPack>
 __global__ void __launch_bounds__(kCopyThreads) copy_batch_kernel(CopyBatch cb) {
-  const int64_t b = blockIdx.x;
+  // the host caps the grid at INT32_MAX blocks: 32-bit block arithmetic
+  const uint32_t b = blockIdx.x;
   int i = 0;
-  while (i + 1 < cb.count && b >= cb.b0[i + 1]) ++i;
-  const int64_t local = b - cb.b0[i];
-  const int r = (int)(local / cb.bx[i]);
+  while (i + 1 < cb.count && b >= (uint32_t)cb.b0[i + 1]) ++i;
+  const uint32_t local = b - (uint32_t)cb.b0[i];
+  const uint32_t bxi = (uint32_t)cb.bx[i];
+  const int r = (int)(local / bxi);
   const int64_t row_units = cb.row_units[i];
   const int64_t slab_rows = cb.slab_rows[i];
   const int32_t* cu = cb.cu[i];
@@ -98,7 +100,7 @@ __global__ void __launch_bounds__(kCopyThreads) copy_batch_kernel(CopyBatch cb) 
   const int64_t real_units = len * row_units;
   const int64_t span_units = (!kPack && cb.zero_tail[i]) ? slab_rows * row_units : real_units;
   constexpr int UN = copy_unroll<kPack>();
-  const int64_t u0 = (local % cb.bx[i]) * units_per_block<kPack>();
+  const int64_t u0 = (int64_t)(local - (uint32_t)r * bxi) * units_per_block<kPack>();
   if (u0 >= span_units) return;
   const u32x4* s = kPack ? cb.src[i] + (int64_t)r * slab_rows * row_units : cb.src[i] + off * row_units;
   u32x4* d = kPack ? cb.dst[i] + off * row_units : cb.dst[i] + (int64_t)r * slab_rows * row_units;
