@@ -10,23 +10,33 @@
 //  * attn_bf16_pp_kernel (varlen, bf16): 8 waves = 256 query rows of one
 //    (request, head), two phase-shifted groups of four so that on each SIMD
 //    one wave issues MFMAs while the other does the softmax; K/V tiles rotate
-//    through three LDS buffers.  With the key split, split_merge_kernel
-//    combines the partial results of the last round's tiles.
-//  * attn_bf16_kernel (block-local, bf16) and attn_f32_kernel (fp32): 4
-//    waves = 128 query rows, keys double-buffered through LDS.
+//    through three LDS buffers.  With a caller workspace, vt_transpose_kernel
+//    first stages V as V^T (the MFMA's V operand then is a plain 16-byte LDS
+//    read) and the last, partial round of tiles is cut along the keys, its
+//    parts combined by split_merge_kernel; without one, V tiles are read
+//    row-major with transposing LDS reads.
+//  * block_local_bf16_kernel / block_local_f32_kernel (block-local, D = 64,
+//    blocks of <= 32 frames): one wave per query block of one (batch, head),
+//    its window in 32-key chunks, V copied straight to LDS.
+//  * block_local_tiled_bf16_kernel (bf16) and attn_f32_kernel (fp32): 4
+//    waves = 128 query rows, keys double-buffered through LDS; the
+//    block-local shapes outside the block-aligned kernels' range, and fp32
+//    varlen.
 //  * every wave owns 32 query rows; Q lives in registers for the whole key
 //    loop.
 //  * S^T = K Q^T on MFMA (bf16: v_mfma_f32_32x32x16_bf16; fp32:
 //    v_mfma_f32_32x32x2_f32), so each lane holds one query's scores for 16
-//    keys and the row max / row sum need one in-lane pass plus one lane-half
-//    swap (v_permlane32_swap).
+//    keys and the row max needs one in-lane pass plus one lane-half swap
+//    (v_permlane32_swap); the row sum likewise, or (ping-pong kernel) a
+//    16x16x32 MFMA over P.
 //  * O^T += V^T P^T on MFMA with P taken straight from the score registers:
 //    the MFMA k-index -> key permutation of the score layout is absorbed by
-//    the order V^T is written to LDS (bf16) or read from LDS (fp32).
+//    the order in which V^T is staged (vt_transpose_kernel), written to LDS,
+//    or read from LDS.
 //  * exp2-domain online softmax with a lazy rescale: the running max used as
 //    the exponent offset only moves when a new score exceeds it by more than
-//    2^8, so most tiles skip the O rescale.  O and l always carry the same
-//    factor, so the ratio is unaffected.
+//    a factor 2^8, so most tiles skip the O rescale.  O and l always carry the
+//    same factor, so the ratio is unaffected.
 //  * varlen masks keys only in a request's last, partial tile; block-local
 //    masks each row to [lo, hi) computed from integers (no dense mask, no
 //    device-to-host decision) and loads only the union of the rows' windows.
@@ -305,15 +315,19 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
-// QB = query blocks of 32 rows per wave, BN = keys per tile.  With QB = 2
-// every K and V operand read from LDS feeds two MFMAs, which halves LDS read
-// traffic per FLOP (LDS bandwidth, especially the transposing V reads, is the
-// co-limiter at 32 rows per wave); such a wave takes one SIMD's whole register
-// file, and 32-key tiles keep its two score buffers within it.
-template <int D, int WAVES, int QB, int BN, bool kBlockLocal>
-__global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf16_kernel(AttnArgs a) {
-  using G = Bf16Geo<D, WAVES, BN>;
-  constexpr int BM = 32 * QB * WAVES;
+// Block-local bf16 attention for the shapes outside the block-aligned
+// kernels' range (D = 128, blocks of more than 32 frames, windows of more
+// than 64 keys): 4 waves = 128 query rows of one (batch row, head).  The keys
+// of the union of the tile rows' windows stream through two LDS buffer pairs
+// in 64-key tiles (K one tile ahead of V), and every row is masked to its own
+// window.  Within a tile step the softmax of this tile's scores is
+// interleaved with the S MFMAs of the next tile, and the row sums with the PV
+// MFMAs.
+template <int D>
+__global__ void __launch_bounds__(256, 2) block_local_tiled_bf16_kernel(AttnArgs a) {
+  constexpr int WAVES = 4;
+  using G = Bf16Geo<D, WAVES, 64>;
+  constexpr int BM = 32 * WAVES;
   // Two separate buffers (not one indexed array) so that the compiler sees
   // the prefetch into one never aliases the reads of the other.
   __shared__ __attribute__((aligned(16))) char k0[G::kTileBytes];
@@ -321,8 +335,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   __shared__ __attribute__((aligned(16))) char k1[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
 
-  const TileRange tr = tile_range<BM, BN, kBlockLocal>(a);
-  if (!tr.valid) return;
+  const TileRange tr = tile_range<BM, G::BN, true>(a);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -333,31 +346,20 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   const int h = tr.h;
   const int64_t row_stride = (int64_t)H * D;  // elements between consecutive tokens
 
-  // Query rows of this lane: block b of the wave covers rows
-  // wave*32*QB + 32b .. +31 of the tile.
-  const int wave_row0 = tr.q0 + wave * 32 * QB;
+  // Query row of this lane: wave*32 + ql of the tile, and its key window.
+  const int wave_row0 = tr.q0 + wave * 32;
   const bool wave_active = wave_row0 < tr.q1;
-  int my_row[QB];
-  int lo[QB], hi[QB];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    my_row[b] = wave_row0 + 32 * b + ql;
-    lo[b] = tr.k_lo;
-    hi[b] = tr.k_hi;
-    if (kBlockLocal) {
-      const int i = min(tr.seq_q0 + wave * 32 * QB + 32 * b + ql, a.n - 1);
-      window_of(a, i, lo[b], hi[b]);
-    }
-  }
+  const int my_row = wave_row0 + ql;
+  int lo, hi;
+  window_of(a, min(tr.seq_q0 + wave * 32 + ql, a.n - 1), lo, hi);
 
   // Q operand of S^T = K Q^T: lane (ql, g) holds features ds*16 + 8g .. +7.
-  bf16x8 qf[QB][G::NDS];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const int qrow = min(my_row[b], tr.q1 - 1);
+  bf16x8 qf[G::NDS];
+  {
+    const int qrow = min(my_row, tr.q1 - 1);
     const bf16x8* qp = (const bf16x8*)((const __bf16*)a.q + (int64_t)qrow * row_stride + (int64_t)h * D + g * 8);
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) qf[b][ds] = qp[2 * ds];
+    for (int ds = 0; ds < G::NDS; ++ds) qf[ds] = qp[2 * ds];
   }
 
   // Direct global -> LDS copy of one tile: wave w's load i fills LDS bytes
@@ -378,7 +380,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   const char* vbase = (const char*)a.v + ((int64_t)tr.kv_base * row_stride + (int64_t)h * D) * 2;
 
   // Buffer descriptors cover only the tile's valid rows, so the hardware
-  // range check returns zeros for rows past the sequence end (their scores
+  // range check returns zeros for rows past the window's end (their scores
   // are masked).  MUBUF loads (not FLAT) keep LDS waits precise.
   auto tile_bytes = [&](int tile) {
     const int valid = min(G::BN, tr.k_hi - (tr.k_lo + tile * G::BN));
@@ -416,27 +418,21 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
     v_rd[db] = v_row * G::ROW + chunk * 16 + (byte_in_row & 15);
   }
 
-  RowState<G::NKB, G::NDB> st[QB];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) st[b].init();
+  RowState<G::NKB, G::NDB> st;
+  st.init();
 
   const int nkeys = tr.k_hi - tr.k_lo;
   const int ntiles = (nkeys + G::BN - 1) / G::BN;
-  const bool ragged = (nkeys % G::BN) != 0;
-  auto is_masked = [&](int tile) { return kBlockLocal || (ragged && tile == ntiles - 1); };
 
-  // ---- S^T = K Q^T.  Step `step` = (ds, kb) with kb fastest; each K
-  // operand feeds the QB query blocks.
+  // ---- S^T = K Q^T.  Step `step` = (ds, kb) with kb fastest.
   constexpr int NSTEP_S = G::NKB * G::NDS;
   constexpr int KPF = 3;  // K operand steps read ahead of their MFMAs
   auto read_k = [&](const char* kl, int step) {
     return *(const bf16x8*)(kl + (step % G::NKB) * 32 * G::ROW + k_rd[step / G::NKB]);
   };
-  auto qk = [&](const char* kl, f32x16(&s)[QB][G::NKB]) {
+  auto qk = [&](const char* kl, f32x16(&s)[G::NKB]) {
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb) s[b][kb] = f32x16{};
+    for (int kb = 0; kb < G::NKB; ++kb) s[kb] = f32x16{};
     bf16x8 ka[KPF + 1];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) ka[i] = read_k(kl, i);
@@ -444,16 +440,14 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
     for (int step = 0; step < NSTEP_S; ++step) {
       if (step + KPF < NSTEP_S) ka[(step + KPF) % (KPF + 1)] = read_k(kl, step + KPF);
       VL_SCHED_BARRIER(0);
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-        s[b][step % G::NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[b][step / G::NKB],
-                                                                     s[b][step % G::NKB], 0, 0, 0);
+      s[step % G::NKB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[step / G::NKB], s[step % G::NKB], 0, 0, 0);
       VL_SCHED_BARRIER(0);
     }
   };
 
-  // ---- Row max of a block's scores and the lazy rescale; returns -offset.
-  auto row_max = [&](RowState<G::NKB, G::NDB>& rs, f32x16(&s)[G::NKB]) {
+  // ---- Row max of the tile's scores and the lazy rescale; returns -offset.
+  auto row_max = [&](f32x16(&s)[G::NKB]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
@@ -461,32 +455,30 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
     mx = pair_max(mx);
     const float mx_c = mx * a.c;
-    const bool need = mx_c > rs.m_c + 8.0f;
+    const bool need = mx_c > st.m_c + 8.0f;
     if (__ballot(need)) {
-      const float m_new = need ? mx_c : rs.m_c;
-      const float alpha = need ? __builtin_amdgcn_exp2f(rs.m_c - m_new) : 1.0f;
-      rs.l *= alpha;
+      const float m_new = need ? mx_c : st.m_c;
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m_c - m_new) : 1.0f;
+      st.l *= alpha;
 #pragma unroll
-      for (int d = 0; d < G::NDB; ++d) rs.o[d] *= alpha;
-      rs.m_c = m_new;
+      for (int d = 0; d < G::NDB; ++d) st.o[d] *= alpha;
+      st.m_c = m_new;
     }
-    return (rs.m_c == -INFINITY) ? 0.f : -rs.m_c;
+    return (st.m_c == -INFINITY) ? 0.f : -st.m_c;
   };
 
-  // ---- exp2 / row sum / bf16 conversion of this tile's scores into the P
-  // operands, interleaved with the S MFMAs of the next tile: per S step, one
-  // K read, QB MFMAs and the VALU work of QB * kScoresPerStep scores.  On a
-  // sequence's last tile the next-tile product reads a stale buffer and is
-  // never used; keeping it makes the exp work and the MFMAs one block.
-  auto softmax_qk = [&](f32x16(&sc)[QB][G::NKB], bf16x8(&pf)[QB][G::NKC], const float(&negm)[QB],
-                        const char* kl_next, f32x16(&sn)[QB][G::NKB], auto&& load_step) {
-    constexpr int kScoresPerStep = G::NKB * 16 / NSTEP_S;  // each lane holds NKB*16 scores per block
+  // ---- exp2 / bf16 conversion of this tile's scores into the P operands,
+  // interleaved with the S MFMAs of the next tile: per S step, one K read,
+  // one MFMA and the VALU work of kScoresPerStep scores.  On the window's
+  // last tile the next-tile product reads a stale buffer and is never used;
+  // keeping it makes the exp work and the MFMAs one block.
+  auto softmax_qk = [&](f32x16(&sc)[G::NKB], bf16x8(&pf)[G::NKC], float negm, const char* kl_next,
+                        f32x16(&sn)[G::NKB], auto&& load_step) {
+    constexpr int kScoresPerStep = G::NKB * 16 / NSTEP_S;  // each lane holds NKB*16 scores
     static_assert(kScoresPerStep * NSTEP_S == G::NKB * 16, "whole scores per step");
     static_assert(NSTEP_S >= 2 * G::kLoadsPerWave, "one tile load per S step at most");
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-      for (int kb = 0; kb < G::NKB; ++kb) sn[b][kb] = f32x16{};
+    for (int kb = 0; kb < G::NKB; ++kb) sn[kb] = f32x16{};
     bf16x8 ka[KPF + 1];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) ka[i] = read_k(kl_next, i);
@@ -494,33 +486,29 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
     for (int step = 0; step < NSTEP_S; ++step) {
       if (step + KPF < NSTEP_S) ka[(step + KPF) % (KPF + 1)] = read_k(kl_next, step + KPF);
       const bool dma = load_step(step);
+      sn[step % G::NKB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[step / G::NKB], sn[step % G::NKB], 0, 0, 0);
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
-        sn[b][step % G::NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[step % (KPF + 1)], qf[b][step / G::NKB],
-                                                                      sn[b][step % G::NKB], 0, 0, 0);
+      for (int t = 0; t < kScoresPerStep; ++t) {
+        const int idx = step * kScoresPerStep + t;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[idx >> 4][idx & 15], a.c, negm));
+        sc[idx >> 4][idx & 15] = p;
+        if ((idx & 7) == 7) {
+          const int kc = idx >> 3;
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int t = 0; t < kScoresPerStep; ++t) {
-          const int idx = step * kScoresPerStep + t;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[b][idx >> 4][idx & 15], a.c, negm[b]));
-          sc[b][idx >> 4][idx & 15] = p;
-          if ((idx & 7) == 7) {
-            const int kc = idx >> 3;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[b][kc][e] = (__bf16)sc[b][kc >> 1][8 * (kc & 1) + e];
-          }
+          for (int e = 0; e < 8; ++e) pf[kc][e] = (__bf16)sc[kc >> 1][8 * (kc & 1) + e];
         }
-      VL_SCHED_GROUP(0x008, QB, 0);                        // the step's MFMAs
+      }
+      VL_SCHED_GROUP(0x008, 1, 0);                         // the step's MFMA
       VL_SCHED_GROUP(0x100, 1, 0);                         // 1 LDS read
       if (dma) VL_SCHED_GROUP(0x020, 1, 0);                // 1 tile load into LDS
       // the scores' VALU work: fma and exp per score, one bf16 pair
       // conversion per two scores
-      VL_SCHED_GROUP(0x002, (2 * kScoresPerStep + kScoresPerStep / 2) * QB, 0);
+      VL_SCHED_GROUP(0x002, 2 * kScoresPerStep + kScoresPerStep / 2, 0);
     }
   };
 
-  // ---- O^T += V^T P^T, V^T operands VPF steps ahead, each feeding QB MFMAs.
+  // ---- O^T += V^T P^T, V^T operands VPF steps ahead.
   auto read_v = [&](const char* vl, int kc, int db) {
     const char* p = vl + kc * 16 * G::ROW + v_rd[db];
     const i16x4 lo4 = lds_read_tr(p);
@@ -530,14 +518,12 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   // The row sums of this tile's probabilities (still in the score registers,
   // which the next tile's scores do not overwrite before its softmax) are
   // added here, a few per MFMA, where the VALU is otherwise idle.
-  auto pv = [&](const char* vl, const bf16x8(&pf)[QB][G::NKC], const f32x16(&sc)[QB][G::NKB]) {
+  auto pv = [&](const char* vl, const bf16x8(&pf)[G::NKC], const f32x16(&sc)[G::NKB]) {
     constexpr int VPF = 6;
     constexpr int NSTEP = G::NKC * G::NDB;
     constexpr int kSumPerStep = G::NKB * 16 / NSTEP;
     static_assert(kSumPerStep * NSTEP == G::NKB * 16, "whole scores per step");
-    float ls[QB][2];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) ls[b][0] = ls[b][1] = 0.f;
+    float ls[2] = {0.f, 0.f};
     bf16x8 va[VPF + 1];
 #pragma unroll
     for (int step = 0; step < VPF; ++step) va[step] = read_v(vl, step / G::NDB, step % G::NDB);
@@ -546,41 +532,31 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
       if (step + VPF < NSTEP)
         va[(step + VPF) % (VPF + 1)] = read_v(vl, (step + VPF) / G::NDB, (step + VPF) % G::NDB);
       VL_SCHED_BARRIER(0);
+      st.o[step % G::NDB] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[step % (VPF + 1)], pf[step / G::NDB], st.o[step % G::NDB], 0, 0, 0);
 #pragma unroll
-      for (int b = 0; b < QB; ++b)
-        st[b].o[step % G::NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            va[step % (VPF + 1)], pf[b][step / G::NDB], st[b].o[step % G::NDB], 0, 0, 0);
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-#pragma unroll
-        for (int t = 0; t < kSumPerStep; ++t) {
-          const int idx = step * kSumPerStep + t;
-          ls[b][t & 1] += sc[b][idx >> 4][idx & 15];
-        }
-        // an opaque use keeps the adds in this step (they would otherwise
-        // sink to the sums' only use after the loop)
-        asm volatile("" : "+v"(ls[b][0]), "+v"(ls[b][1]));
+      for (int t = 0; t < kSumPerStep; ++t) {
+        const int idx = step * kSumPerStep + t;
+        ls[t & 1] += sc[idx >> 4][idx & 15];
       }
+      // an opaque use keeps the adds in this step (they would otherwise
+      // sink to the sums' only use after the loop)
+      asm volatile("" : "+v"(ls[0]), "+v"(ls[1]));
       VL_SCHED_BARRIER(0);
     }
-#pragma unroll
-    for (int b = 0; b < QB; ++b) st[b].l += ls[b][0] + ls[b][1];
+    st.l += ls[0] + ls[1];
   };
 
   // One tile: S of this tile is in sc; K of the next tile is in kl_next
   // (when there is one), V of this tile in vl.
-  bf16x8 pf[QB][G::NKC];
+  bf16x8 pf[G::NKC];
   // The wave's share of the next tiles' loads (K of tile kt into kdst, V of
   // tile vt into vdst; -1 = none) is spread one load per S step so the
   // copies stream while the MFMAs run instead of stalling issue in a burst.
-  auto tile_step = [&](int tile, f32x16(&sc)[QB][G::NKB], f32x16(&sn)[QB][G::NKB], const char* kl_next,
-                       const char* vl, int kt, char* kdst, int vt, char* vdst) {
-    float negm[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      if (is_masked(tile)) mask_scores<G::NKB>(sc[b], tr.k_lo + tile * G::BN, g, lo[b], hi[b]);
-      negm[b] = row_max(st[b], sc[b]);
-    }
+  auto tile_step = [&](int tile, f32x16(&sc)[G::NKB], f32x16(&sn)[G::NKB], const char* kl_next, const char* vl,
+                       int kt, char* kdst, int vt, char* vdst) {
+    mask_scores<G::NKB>(sc, tr.k_lo + tile * G::BN, g, lo, hi);
+    const float negm = row_max(sc);
     // No next tile (kt or vt < 0): the copy still issues, with a zero-byte
     // descriptor, so it reads nothing; its destination buffer is not read
     // during this step.  Keeping it unconditional keeps the whole step one
@@ -608,7 +584,7 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   // K runs one tile ahead of V: during tile t the waves read K(t+1) and V(t)
   // while K(t+2) and V(t+1) stream into the buffers that held K(t) and
   // V(t-1); one barrier per tile separates the two.
-  f32x16 sA[QB][G::NKB], sB[QB][G::NKB];
+  f32x16 sA[G::NKB], sB[G::NKB];
   if (ntiles > 0) {
     issue_k(0, k0);
     issue_v(0, v0);
@@ -647,49 +623,23 @@ __global__ void __launch_bounds__(64 * WAVES, (QB == 1 ? 8 / WAVES : 1)) attn_bf
   }
 
   if (!wave_active) return;
-  if (!kBlockLocal && tr.unit >= 0) {
-    // Split work item: unnormalised O, the exponent offset and the row sum
-    // go to the unit's partial-result slot for the merge kernel.
-    float* wo = a.ws + (int64_t)tr.unit * BM * D;
-    float2* wml = (float2*)(a.ws + (int64_t)a.slots * BM * D) + (int64_t)tr.unit * BM;
+  const float l_tot = pair_sum(st.l);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (my_row < tr.q1) {
+    __bf16* op = (__bf16*)a.out + (int64_t)my_row * row_stride + (int64_t)h * D;
 #pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const float l_tot = pair_sum(st[b].l);
-      if (my_row[b] < tr.q1) {
-        const int r = my_row[b] - tr.q0;
+    for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db)
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + 8 * i + 4 * g;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 w;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = db * 32 + 8 * i + 4 * g;
-            *(f32x4*)(wo + (int64_t)r * D + d) =
-                f32x4{st[b].o[db][4 * i], st[b].o[db][4 * i + 1], st[b].o[db][4 * i + 2], st[b].o[db][4 * i + 3]};
-          }
-        if (g == 0) wml[r] = make_float2(st[b].m_c, l_tot);
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[db][4 * i + e] * inv);
+        *(bf16x4*)(op + d) = w;
       }
-    }
-    return;
-  }
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const float l_tot = pair_sum(st[b].l);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (my_row[b] < tr.q1) {
-      __bf16* op = (__bf16*)a.out + (int64_t)my_row[b] * row_stride + (int64_t)h * D;
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = db * 32 + 8 * i + 4 * g;
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st[b].o[db][4 * i + e] * inv);
-          *(bf16x4*)(op + d) = w;
-        }
-      if (a.lse != nullptr && g == 0)
-        a.lse[(int64_t)my_row[b] * H + h] = l_tot > 0.f ? (st[b].m_c + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(int64_t)my_row * H + h] = l_tot > 0.f ? (st.m_c + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -702,9 +652,9 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 
 // Varlen bf16 attention with 8 waves in two groups of four.  Waves w and
 // w + 4 share a SIMD, so each SIMD runs one wave of each group.  A wave
-// handles tile t in two phases: an MFMA phase (O += V(t-1)^T P(t-1)^T, then
-// S(t) = K(t) Q^T: 32 MFMAs) and a VALU phase (mask, row max, lazy rescale,
-// exp2, row sum and bf16 pack of P(t)).  Group 1 runs one phase behind group
+// handles tile t in two phases: an MFMA phase (O += V(t-1)^T P(t-1)^T with
+// the row sums of P(t-1), then S(t) = K(t) Q^T: 36 MFMAs) and a VALU phase
+// (mask, row max, lazy rescale, exp2 and bf16 pack of P(t)).  Group 1 runs one phase behind group
 // 0 and every phase ends at a work-group barrier, so on each SIMD one wave
 // issues MFMAs while the other does the softmax arithmetic.
 // K and V tiles rotate through three LDS buffers each.  In phase 2j the
@@ -1555,15 +1505,6 @@ __global__ void __launch_bounds__(256, 3) block_local_bf16_kernel(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- split merge
-
-// Merges the partial results of the split work items.  Tail tile t's key
-// ranges ran as units t*parts .. t*parts + parts - 1; a block handles RPB rows
-// of one tail tile, a thread one 4-float group of a row.  Per row, with
-// exponent offsets m_p (log2 units) and row sums l_p of the parts:
-// m = max m_p, w_p = 2^(m_p - m), out = sum_p w_p O_p / sum_p w_p l_p,
-// lse = (m + log2 sum_p w_p l_p) ln 2 -- taken in one pass over the parts with
-// a running maximum.  Empty parts carry m_p = -inf, l_p = 0 and are skipped.
 // ---------------------------------------------------------------- V^T staging
 
 // One 64-key tile of one head of V -> V^T: V rows [T, H, D] (bf16) of request
@@ -1628,6 +1569,15 @@ __global__ void __launch_bounds__(256) vt_transpose_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- split merge
+
+// Merges the partial results of the split work items.  Tail tile t's key
+// ranges ran as units t*parts .. t*parts + parts - 1; a block handles RPB rows
+// of one tail tile, a thread one 4-float group of a row.  Per row, with
+// exponent offsets m_p (log2 units) and row sums l_p of the parts:
+// m = max m_p, w_p = 2^(m_p - m), out = sum_p w_p O_p / sum_p w_p l_p,
+// lse = (m + log2 sum_p w_p l_p) ln 2 -- taken in one pass over the parts with
+// a running maximum.  Empty parts carry m_p = -inf, l_p = 0 and are skipped.
 template <int D, int BM>
 __global__ void __launch_bounds__(256) split_merge_kernel(AttnArgs a) {
   constexpr int C4 = D / 4;         // 4-float groups per row
@@ -1948,9 +1898,9 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
       hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 2>), ag, dim3(256), 0, stream, a);
   } else {
     if (D == 128)
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<128, 4, 1, 64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::block_local_tiled_bf16_kernel<128>), dim3((unsigned)G), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((vl::attn_bf16_kernel<64, 4, 1, 64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::block_local_tiled_bf16_kernel<64>), dim3((unsigned)G), dim3(256), 0, stream, a);
   }
   return launch_status();
 }
