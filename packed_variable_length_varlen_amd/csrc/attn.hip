@@ -1221,9 +1221,14 @@ struct BlockUnit {
   int b, h, r0, nq, k_lo, k_hi;
 };
 
-// Grid (ceil(nb / 4), H, B): wave w of work-group x takes query block 4x + w
-// (neighbouring blocks, which share keys, in neighbouring waves) of head y
-// and batch row z.
+// Grid (ceil(nb / kBlockWaves), H, B): wave w of work-group x takes query
+// block kBlockWaves * x + w (neighbouring blocks, which share keys, in
+// neighbouring waves) of head y and batch row z.  Two-wave work-groups: the
+// vocoder shape's 1,344 waves then reach the 256 CUs as 672 small groups
+// rather than 336 of four, which spreads them evenly (-7 to -10 % at the
+// vocoder shape, -1 to -3 % at the production shape, against four waves;
+// one wave per group measured about the same as two, eight slower).
+constexpr int kBlockWaves = 2;
 __device__ __forceinline__ BlockUnit block_unit(const AttnArgs& a, int qb, int nb) {
   BlockUnit u;
   u.h = blockIdx.y;
@@ -1254,23 +1259,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 //   copied straight to LDS (256-byte rows; rows 4..7 of each group of 8 have
 //   their two 128-byte halves swapped, so the two lane halves of a read --
 //   rows 4 apart -- hit different banks) and each operand is one 4-byte read.
-// One LDS buffer per wave (32 KB per work-group): the next chunk's V copy
-// starts after this chunk's PV reads, and three waves fit on each SIMD (162
-// VGPRs); double-buffering V (64 KB per work-group, two waves per SIMD) was
+// One LDS buffer per wave (8 KB): the next chunk's V copy starts after this
+// chunk's PV reads, and three waves fit on each SIMD (162 VGPRs);
+// double-buffering V (two waves per SIMD) was
 // slower at every window.
 template <int D>
-__global__ void __launch_bounds__(256, 3) block_local_f32_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * kBlockWaves, 3) block_local_f32_kernel(AttnArgs a) {
   static_assert(D == 64, "two lane halves of 32 features");
   constexpr int NQ = D / 2;
   constexpr int NDB = D / 32;
   constexpr int VCH = 32 * D * 4;  // bytes of one chunk of V in LDS
-  __shared__ __attribute__((aligned(16))) char vlds[4][VCH];
+  __shared__ __attribute__((aligned(16))) char vlds[kBlockWaves][VCH];
   const int lane = threadIdx.x & 63;
   const int ql = lane & 31;
   const int g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = (a.n + a.block - 1) / a.block;
-  const int qb = blockIdx.x * 4 + wave;
+  const int qb = blockIdx.x * kBlockWaves + wave;
   if (qb >= nb) return;
   const BlockUnit u = block_unit(a, qb, nb);
   const int rs = a.H * D * 4;  // bytes between consecutive frames
@@ -1383,20 +1388,20 @@ __global__ void __launch_bounds__(256, 3) block_local_f32_kernel(AttnArgs a) {
 // NBUF = 2 for windows of two chunks: the next chunk's V streams into the
 // other LDS buffer while this one computes; 1 for single-chunk windows.
 template <int D, int NBUF>
-__global__ void __launch_bounds__(256, 3) block_local_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * kBlockWaves, 3) block_local_bf16_kernel(AttnArgs a) {
   static_assert(D == 64, "four 16-feature MFMA steps");
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int ROW = D * 2;
   constexpr int CPR = D / 8;
   constexpr int VCH = 32 * ROW;
-  __shared__ __attribute__((aligned(16))) char vlds[4][NBUF][VCH];
+  __shared__ __attribute__((aligned(16))) char vlds[kBlockWaves][NBUF][VCH];
   const int lane = threadIdx.x & 63;
   const int ql = lane & 31;
   const int g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nb = (a.n + a.block - 1) / a.block;
-  const int qb = blockIdx.x * 4 + wave;
+  const int qb = blockIdx.x * kBlockWaves + wave;
   if (qb >= nb) return;
   const BlockUnit u = block_unit(a, qb, nb);
   const int rs = a.H * D * 2;
@@ -1883,9 +1888,9 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
                        B <= 65535;
   const bool one_chunk = window <= 32;
   const int64_t nblk = (n + block - 1) / block;
-  const dim3 ag((unsigned)((nblk + 3) / 4), (unsigned)H, (unsigned)B);
+  const dim3 ag((unsigned)((nblk + vl::kBlockWaves - 1) / vl::kBlockWaves), (unsigned)H, (unsigned)B);
   if (kF32 && aligned) {
-    hipLaunchKernelGGL((vl::block_local_f32_kernel<64>), ag, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((vl::block_local_f32_kernel<64>), ag, dim3(64 * vl::kBlockWaves), 0, stream, a);
   } else if (kF32) {
     if (D == 128)
       hipLaunchKernelGGL((vl::attn_f32_kernel<128, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
@@ -1893,9 +1898,9 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
   } else if (aligned && window <= 64) {
     if (one_chunk)
-      hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 1>), ag, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 1>), ag, dim3(64 * vl::kBlockWaves), 0, stream, a);
     else
-      hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 2>), ag, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 2>), ag, dim3(64 * vl::kBlockWaves), 0, stream, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL((vl::block_local_tiled_bf16_kernel<128>), dim3((unsigned)G), dim3(256), 0, stream, a);
