@@ -1385,8 +1385,10 @@ __global__ void __launch_bounds__(64 * kBlockWaves, 3) block_local_f32_kernel(At
 //   straight to LDS (128-byte rows, 16-byte chunks XOR-swizzled by row) and
 //   the V^T operands read back with two transposing reads each
 //   (ds_read_b64_tr_b16), which deliver exactly those keys of one feature.
-// NBUF = 2 for windows of two chunks: the next chunk's V streams into the
-// other LDS buffer while this one computes; 1 for single-chunk windows.
+// NBUF = 2 for windows of two or three chunks (a ring of two buffers: the
+// next chunk's V streams into the other one while this one computes; a
+// buffer is refilled only after the PV reads of the chunk it held have
+// returned), 1 for single-chunk windows.
 template <int D, int NBUF>
 __global__ void __launch_bounds__(64 * kBlockWaves, 3) block_local_bf16_kernel(AttnArgs a) {
   static_assert(D == 64, "four 16-feature MFMA steps");
@@ -1896,7 +1898,12 @@ int block_local_common(const void* q, const void* k, const void* v, int32_t B, i
       hipLaunchKernelGGL((vl::attn_f32_kernel<128, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, true>), dim3((unsigned)G), dim3(256), 0, stream, a);
-  } else if (aligned && window <= 64) {
+  } else if (aligned && window <= 96) {
+    // Wider windows go to the tiled kernel, which shares the keys of 128
+    // queries' windows through LDS, where each wave here re-reads its own
+    // window: at 4-5 chunks the tiled kernel is faster at the production
+    // shape (B = 2, n = 4000) though not yet at the vocoder's (B = 1,
+    // n = 2003), and the 96-key limit is faster at both.
     if (one_chunk)
       hipLaunchKernelGGL((vl::block_local_bf16_kernel<64, 1>), ag, dim3(64 * vl::kBlockWaves), 0, stream, a);
     else
