@@ -4,9 +4,11 @@
  * All tensor pointers are DEVICE pointers owned by the caller.  Every function
  * enqueues its work on `stream` and returns at once: no allocation, no
  * host<->device copy or synchronisation.  The library keeps no global mutable
- * state with one exception: a per-device cache of one occupancy query
+ * state with two exceptions: a per-device cache of one occupancy query
  * (resident work-groups of the attention kernel, read once, mutex-guarded),
- * which sizes the key split of varlen_attn_fwd_split.  Device-
+ * which sizes the key split of varlen_attn_fwd_split, and the static device
+ * scratch array of varlen_attn_fwd_noalloc with its per-device address
+ * (looked up once, mutex-guarded; see that function).  Device-
  * resident cu_seqlens are trusted preconditions (checking them would need a
  * device-to-host read); host scalars are validated and a bad one returns an
  * error code before anything is launched.  Return value: VL_OK (0) on success,

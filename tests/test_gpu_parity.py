@@ -685,6 +685,37 @@ def test_block_local_random_shapes(case, f32):
     check_lse(to64(lse), rl, f32, f"block-local random {case}", rounded_weights=False)
 
 
+# Windows at the edges of the kernel choice: D = 64 blocks of <= 32 frames
+# take the one-wave-per-block kernels (bf16 up to 96 keys: one, two or three
+# 32-key chunks; fp32 at any width), the rest the tiled kernels.  (block,
+# look_back, look_ahead): 96 keys in three whole chunks, 93 and 95 keys with
+# a ragged last chunk, 97 and 128 keys on the tiled side, 32 keys in one
+# chunk and 33 in two; n leaves a ragged last block and clips the windows at
+# both ends.
+BL_EDGES = [(32, 1, 1), (31, 1, 1), (19, 2, 2), (97, 0, 0), (32, 2, 1), (32, 0, 0), (33, 0, 0), (11, 1, 1)]
+
+
+@pytest.mark.parametrize("edge", BL_EDGES)
+@pytest.mark.parametrize("f32", [False, True])
+def test_block_local_window_edges(edge, f32):
+    block, lb, la = edge
+    B, n, H = 2, 7 * block + block // 2 + 1, 3
+    dtype = torch.float32 if f32 else torch.bfloat16
+    log(f"[block_local] window edge block={block} lb={lb} la={la} ({(1 + lb + la) * block} keys) n={n} {dtype}")
+    rng = np.random.default_rng(block * 7 + lb * 3 + la)
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, n, H, 64)).astype(np.float32)).to(dtype) for _ in range(3))
+    fn = vl.block_local_attn_fwd_f32 if f32 else vl.block_local_attn_fwd
+    full, out = canary_out(tuple(q.shape), dtype, pad=1)
+    lse_full, lse = canary_out((B, n, H), torch.float32, pad=1)
+    fn(q.to(DEV), k.to(DEV), v.to(DEV), block, lb, la, 0.125, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert_canary(full, pad=1)
+    assert_canary(lse_full, pad=1)
+    ro, rl = oracle.block_local_attention(to64(q), to64(k), to64(v), block, lb, la, 0.125)
+    check_close(to64(out), ro, f32, f"block-local edge {edge}")
+    check_lse(to64(lse), rl, f32, f"block-local edge {edge}", rounded_weights=False)
+
+
 @pytest.mark.parametrize("f32", [False, True])
 def test_block_local_own_block_agrees_with_varlen_on_block_requests(f32):
     """Own-block windows with n a multiple of the block are varlen attention
