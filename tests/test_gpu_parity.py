@@ -438,6 +438,46 @@ def _split_parts(ql, kl, H, D):
     return oracle.split_plan(T, slots, max(kl)), slots
 
 
+def _varlen_random_cases(seed: int, count: int):
+    """Seeded random packed batches: 1-6 requests of 0-1200 query rows (some
+    empty), keys equal to the queries or drawn apart (0-1500, some empty),
+    1-4 heads, D of 64 or 128."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        R = int(rng.integers(1, 7))
+        ql = [0 if rng.random() < 0.15 else int(rng.integers(1, 1201)) for _ in range(R)]
+        if rng.random() < 0.6:
+            kl = list(ql)
+        else:
+            kl = [0 if rng.random() < 0.1 else int(rng.integers(1, 1501)) for _ in range(R)]
+        cases.append((ql, kl, int(rng.integers(1, 5)), int(rng.choice([64, 128]))))
+    return cases
+
+
+VL_RANDOM = _varlen_random_cases(91, 10)
+
+
+@pytest.mark.parametrize("case", VL_RANDOM, ids=[f"R{len(c[0])}-H{c[2]}-D{c[3]}-{i}" for i, c in enumerate(VL_RANDOM)])
+def test_varlen_random_batches(case):
+    """Each random batch through the three launches (bf16, bf16 with the
+    workspace: staged V^T and the key split of the last round, fp32), every
+    output row and lse against the oracle, canaries around both."""
+    ql, kl, H, D = case
+    log(f"[varlen] random ql={ql} kl={kl} H={H} D={D}")
+    q_cu = oracle.cu_seqlens_from_lengths(ql)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    scale = wl.softmax_scale(D)
+    for f32, split in ((False, False), (False, True), (True, False)):
+        dtype = torch.float32 if f32 else torch.bfloat16
+        q, k, v = wl.random_varlen_case(sum(ql) + 7 * sum(kl) + D, ql, H, D, dtype, kl)
+        out, lse = _run_varlen(q, k, v, q_cu, kv_cu, scale, f32, split=split)
+        ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), q_cu, kv_cu, scale)
+        what = f"random {case} {'f32' if f32 else 'bf16'}{' split' if split else ''}"
+        check_close(to64(out), ro, f32, what)
+        check_lse(to64(lse), rl, f32, what)
+
+
 SPLIT_CASES = [
     # one round only: every tile is cut
     ("one_request", [3000], None, 2, 128),
