@@ -168,7 +168,7 @@ int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
 
 /* varlen_attn_fwd_split: varlen_attn_fwd (same contract; results equal up to
  *   fp32 summation order and the order of the keys inside each MFMA step)
- *   with a caller-provided workspace that serves two purposes.
+ *   with a caller-provided workspace that serves three purposes.
  *   1. V^T staging: a first kernel writes V transposed, per head D rows of
  *      vt_ld = roundup(kv_rows, 64) + 64 * num_reqs bf16 columns, request r's
  *      keys from column 64 * (ceil(kv_cu_seqlens[r] / 64) + r), each request
@@ -183,11 +183,24 @@ int varlen_attn_fwd_f32(const float* q, const float* k, const float* v,
  *      whole 64-key tiles, run as separate work-groups that write
  *      unnormalised partial results to the workspace; a last kernel on the
  *      same stream merges them (log-sum-exp weights) into out / lse.
+ *   3. Chiplet work queues: the work items the static schedule below deals
+ *      to each of the 8 chiplets form that chiplet's queue, in the same
+ *      order; a work-group takes the next item of its own chiplet's queue
+ *      (an atomic ticket on a counter in the workspace, zeroed by the V^T
+ *      staging kernel) and, once that queue is empty, the next item of
+ *      another queue, so chiplets that run at a higher clock take on more
+ *      of the work.  The launch has an eighth more work-groups than the
+ *      item bound for that; work-groups that find every queue empty exit.
+ *      Which work-group runs an item does not change its result: out and
+ *      lse are the same bits from call to call.
  *   kv_rows: rows of k and v (>= kv_cu_seqlens[num_reqs]; the Python binding
  *   passes k.shape[0]); it sizes the V^T rows.
  *   workspace: device, 16-byte aligned, at least the bytes
- *   varlen_split_workspace_bytes reports for (kv_rows, num_reqs, H, D); its
- *   contents need no initialisation and are scratch after the call.  Two
+ *   varlen_split_workspace_bytes reports for (kv_rows, num_reqs, H, D): the
+ *   partial results (slots * 256 * (4 * D + 8) bytes, rounded up to 256),
+ *   V^T (H * D * vt_ld * 2 bytes, rounded up to 256), then 256 bytes of
+ *   queue counters; its contents need no initialisation and are scratch
+ *   after the call.  Two
  *   calls that share a workspace must be ordered (same stream, or
  *   synchronised).  A missing or short workspace returns VL_EINVAL; a V^T
  *   row of more than 2^31 bytes (D * vt_ld * 2) returns VL_EUNSUPPORTED.
@@ -205,7 +218,8 @@ int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, i
  *   (code under HIP graph capture, tight serving loops, harnesses that forbid
  *   hipMalloc).  Same arguments and contract as varlen_attn_fwd; it runs the
  *   key split of the last round like varlen_attn_fwd_split, with the same
- *   split plan, but keeps the partial results in a static device array of
+ *   split plan but the static schedule (no chiplet queues), and keeps the
+ *   partial results in a static device array of
  *   VL_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends) and reads V
  *   row-major (no V^T staging, whose buffer grows with the input); its out and
  *   lse are the same bits as varlen_attn_fwd_split's.  It calls no hipMalloc
@@ -264,13 +278,17 @@ int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chu
  *   split = 0), varlen_attn_fwd_split (dtype_f32 = 0, split = 1) or
  *   varlen_attn_fwd_f32 (dtype_f32 = 1) uses for these scalars: query rows
  *   per work-group (block_m), chiplet chunk, number of work-groups and the
- *   slot count of the key split (0 = no split possible).  Any output pointer
- *   may be NULL.
+ *   slot count of the key split (0 = no split possible).  The split = 1
+ *   launch adds spare work-groups for its chiplet queues: an eighth of the
+ *   item bound (R * H * ceil(max_q / block_m) + slots) before the rounding
+ *   up to whole groups of 8 * chunk.  Any output pointer may be NULL.
  * varlen_tile_map: writes, for every launched work-group b of that launch,
  *   (request, head, q-tile, part, parts) into items_out[5*b .. 5*b+4]:
  *   part 0 of 1 for a whole tile, key range `part` of `parts` for a split
  *   one, all -1 for an idle work-group; it runs the same device code as the
- *   attention kernel.  items_out: int32 [max_blocks, 5] (device); max_blocks
+ *   attention kernel.  For split = 1 it gives the static map, which is also
+ *   each chiplet queue's order: the item each work-group takes while every
+ *   chiplet keeps to its own queue in work-group order.  items_out: int32 [max_blocks, 5] (device); max_blocks
  *   must be >= the launch size, else VL_EINVAL.
  *   Schedule: requests by key length descending (ties: lower index first) when
  *   num_reqs <= 64, else in index order; heads ascending; q-tiles ascending.

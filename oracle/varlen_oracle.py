@@ -253,11 +253,14 @@ def split_range(nkt: int, part: int, parts: int) -> Tuple[int, int]:
 
 
 def grid_blocks(num_reqs: int, max_q: int, H: int, block_m: int, chunk: int, xcds: int = XCDS,
-                slots: int = 0) -> int:
+                slots: int = 0, queues: bool = False) -> int:
     """Launch size the host derives from scalars only: an upper bound on the
-    tile count plus one round of slots when the key split is on, rounded up
-    to a whole number of (xcds x chunk) groups."""
+    tile count plus one round of slots when the key split is on, plus (with
+    the chiplet work queues of the workspace launch) an eighth of that bound
+    in spare blocks, rounded up to a whole number of (xcds x chunk) groups."""
     upper = num_reqs * H * ((max_q + block_m - 1) // block_m) + max(slots, 0)
+    if queues:
+        upper += (upper + 7) // 8
     group = xcds * chunk
     return ((upper + group - 1) // group) * group
 
@@ -275,6 +278,19 @@ def block_to_logical(b: int, chunk: int, xcds: int = XCDS) -> int:
     return ((i // chunk) * xcds + x) * chunk + (i % chunk)
 
 
+def chiplet_queues(n_items: int, chunk: int, xcds: int = XCDS) -> List[List[int]]:
+    """The chiplet work queues of the workspace launch: queue x lists, in
+    order, the logical items [0, n_items) that block_to_logical deals to the
+    blocks of chiplet x (its k-th block's item is the queue's k-th entry).  A
+    block takes the next entry of its own chiplet's queue, or of another queue
+    once its own is empty; which block runs an item decides nothing about the
+    item's result."""
+    queues: List[List[int]] = [[] for _ in range(xcds)]
+    for t in range(n_items):
+        queues[(t // chunk) % xcds].append(t)
+    return queues
+
+
 def work_items(q_cu, kv_cu, H: int, block_m: int, slots: int = 0, max_kv: int = 0,
                lpt_max_reqs: int = LPT_MAX_REQS) -> List[Tuple[int, int, int, int, int]]:
     """Logical list of (request, head, q-tile, part, parts) work items: the
@@ -290,11 +306,13 @@ def work_items(q_cu, kv_cu, H: int, block_m: int, slots: int = 0, max_kv: int = 
 
 def block_schedule(q_cu, kv_cu, H: int, block_m: int, max_q: int, chunk: int,
                    lpt_max_reqs: int = LPT_MAX_REQS, xcds: int = XCDS, slots: int = 0,
-                   max_kv: int = 0) -> np.ndarray:
-    """(request, head, q-tile, part, parts) of every launched block, all -1 if idle."""
+                   max_kv: int = 0, queues: bool = False) -> np.ndarray:
+    """(request, head, q-tile, part, parts) of every launched block, all -1 if
+    idle: the static map (with the chiplet queues, the item each block takes
+    while every chiplet keeps to its own queue in block order)."""
     items = work_items(q_cu, kv_cu, H, block_m, slots, max_kv, lpt_max_reqs)
     R = len(validate_cu_seqlens(q_cu)) - 1
-    G = grid_blocks(R, max_q, H, block_m, chunk, xcds, slots)
+    G = grid_blocks(R, max_q, H, block_m, chunk, xcds, slots, queues)
     out = np.full((G, 5), -1, dtype=np.int64)
     for b in range(G):
         t = block_to_logical(b, chunk, xcds)

@@ -378,8 +378,9 @@ def varlen_attn_fwd_split(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, s
                           lse=None, workspace: Optional[torch.Tensor] = None, padded_tokens: int = 0,
                           attn_mask=None, return_lse: bool = False, stream=None,
                           check_cu_seqlens: bool = False):
-    """varlen_attn_fwd through a workspace: V is staged transposed there, and
-    the last partial round is cut along the keys.  `workspace` (a device
+    """varlen_attn_fwd through a workspace: V is staged transposed there, the
+    last partial round is cut along the keys, and the work items are taken
+    through per-chiplet queues (counters in the workspace).  `workspace` (a device
     buffer of varlen_split_workspace_bytes(k.shape[0], num_reqs, H, D) bytes)
     is allocated when not given."""
     return _varlen("varlen_attn_fwd_split", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,

@@ -77,6 +77,9 @@ struct AttnArgs {
   // keys from column vt_col_base(kv_cu[r], r) (nullptr: read V directly)
   void* vt;
   int64_t vt_ld;
+  // chiplet work queues of the workspace launch: kXcds ticket counters
+  // (zeroed by the V^T staging kernel); nullptr = the static block map
+  int* dyn;
 };
 
 // ---------------------------------------------------------------- tile setup
@@ -92,13 +95,20 @@ struct TileRange {
   bool valid;
 };
 
+// logical_item: the varlen work item this work-group takes (-1: none), or
+// kStaticItem for the static block map.
+constexpr int kStaticItem = -2;
 template <int BM, int BN, bool kBlockLocal>
-__device__ __forceinline__ TileRange tile_range(const AttnArgs& a) {
+__device__ __forceinline__ TileRange tile_range(const AttnArgs& a, int logical_item = kStaticItem) {
   TileRange t;
   t.valid = true;
   t.unit = -1;
   if (!kBlockLocal) {
-    const int logical = block_to_logical(blockIdx.x, a.chunk);
+    const int logical = logical_item == kStaticItem ? block_to_logical(blockIdx.x, a.chunk) : logical_item;
+    if (logical < 0) {
+      t.valid = false;
+      return t;
+    }
     const WorkItem w = work_item(a.q_cu, a.kv_cu, a.R, a.H, BM, a.slots, a.max_kv, logical);
     if (w.req < 0) {
       t.valid = false;
@@ -645,6 +655,42 @@ __global__ void __launch_bounds__(256, 2) block_local_tiled_bf16_kernel(AttnArgs
 
 // ---------------------------------------------------------------- bf16 ping-pong kernel
 
+// Chiplet work queues (the workspace launch).  The chiplets of one device
+// run at different clocks (the card sits at its power limit; 1.58-1.80 GHz
+// measured per chiplet), so a fixed share of the work per chiplet leaves the
+// fast ones idle at the end.  Queue x holds, in order, exactly the logical
+// items the static map gives chiplet x: item k of the queue is logical
+// ((k div chunk) * 8 + x) * chunk + k mod chunk, the item of the k-th block
+// on that chiplet.  A work-group takes the next item of its own chiplet's
+// queue with one atomic ticket and, once that queue is empty, the next item
+// of another queue that still has some, so faster chiplets take on more of
+// the work while each run of `chunk` items (one request and head: the same
+// K/V) still starts on one chiplet.  Lane j < 8 holds c, its read of queue
+// x + j's counter; only queues that still had items get a ticket request, so
+// the spare work-groups past the last item take no atomic.  Returns the
+// logical item, or -1 when every queue is empty.  n_items: logical items of
+// the launch.  Called by a whole wave; the result is wave-uniform.  At most
+// eight tickets are tried: no work-group waits on another.
+__device__ __forceinline__ int queue_len(int n_items, int chunk, int y) {
+  const int per8 = kXcds * chunk;
+  const int full = n_items / per8;
+  return full * chunk + min(chunk, max(0, n_items - full * per8 - y * chunk));
+}
+__device__ __forceinline__ int take_item(int* cnt, int n_items, int chunk, int x, int c) {
+  const int lane = lane_id();
+  uint64_t avail = __ballot(lane < kXcds && c < queue_len(n_items, chunk, (x + lane) % kXcds));
+  while (avail != 0) {
+    const int j = __ffsll((unsigned long long)avail) - 1;  // own queue first, then the next ones
+    const int qy = (x + j) % kXcds;
+    int k = 0;
+    if (lane == 0) k = atomicAdd(cnt + qy, 1);
+    k = __builtin_amdgcn_readfirstlane(k);
+    if (k < queue_len(n_items, chunk, qy)) return ((k / chunk) * kXcds + qy) * chunk + k % chunk;
+    avail &= ~(1ull << j);
+  }
+  return -1;
+}
+
 // Work-group barrier without a memory fence: LDS copies are waited for
 // explicitly (vmcnt) before it, and the "memory" clobber keeps the compiler
 // from moving loads or stores across it.
@@ -683,7 +729,27 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char v2[G::kTileBytes];
 
-  const TileRange tr = tile_range<BM, BN, false>(a);
+  int logical = kStaticItem;
+  if (a.dyn != nullptr) {
+    __shared__ int item_s;
+    if (threadIdx.x < 64) {
+      const int x = (int)(blockIdx.x % kXcds);
+      int c = 0;
+      if (threadIdx.x < kXcds)
+        c = __hip_atomic_load(a.dyn + (x + threadIdx.x) % kXcds, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int T = total_tiles(a.q_cu, a.R, a.H, BM);
+      int n_items = T;
+      if (a.slots > 0) {
+        const SplitPlan sp = split_plan(T, a.slots, a.max_kv);
+        if (sp.parts > 1) n_items = sp.full + sp.tail * sp.parts;
+      }
+      const int it = take_item(a.dyn, n_items, a.chunk, x, c);
+      if (threadIdx.x == 0) item_s = it;
+    }
+    __syncthreads();
+    logical = item_s;
+  }
+  const TileRange tr = tile_range<BM, BN, false>(a, logical);
   if (!tr.valid) return;
 
   const int tid = threadIdx.x;
@@ -1527,6 +1593,8 @@ __global__ void __launch_bounds__(256) vt_transpose_kernel(AttnArgs a) {
   constexpr int LD = D + 2;  // bf16 per LDS row: an odd dword count, so column reads spread over banks
   constexpr int CPR = D / 8;
   __shared__ uint32_t sm[kVtTile * LD / 2];
+  // the attention kernel that follows starts its chiplet queues from zero
+  if (a.dyn != nullptr && blockIdx.x == 0 && threadIdx.x < kXcds) a.dyn[threadIdx.x] = 0;
   const int ntc = (int)(a.vt_ld / kVtTile);
   const int h = blockIdx.x / ntc;
   const int64_t col0 = (int64_t)(blockIdx.x % ntc) * kVtTile;
@@ -1700,28 +1768,42 @@ struct VarlenPlan {
   int block_m;
   int threads;
   int slots;
+  bool queues;
   int64_t blocks;
 };
 
-inline VarlenPlan varlen_plan(bool f32, bool split, int64_t num_reqs, int64_t max_q, int64_t max_kv, int64_t H,
-                              int D) {
+// queues: the launch takes its items through the chiplet work queues (the
+// workspace launch); it then gets an eighth more work-groups than the item
+// bound, so that chiplets that run faster have work-groups left with which
+// to take other chiplets' items.
+inline VarlenPlan varlen_plan(bool f32, bool split, bool queues, int64_t num_reqs, int64_t max_q, int64_t max_kv,
+                              int64_t H, int D) {
   VarlenPlan p;
   p.block_m = f32 ? 32 * kF32Waves : kBf16VarlenBM;
   p.threads = f32 ? 64 * kF32Waves : kBf16VarlenThreads;
   // a split needs at least two key ranges of kMinSplitKeys keys
   p.slots = (split && !f32 && max_kv / vl::kMinSplitKeys >= 2) ? bf16_varlen_slots(D) : 0;
-  p.blocks = (num_reqs == 0 || max_q == 0) ? 0 : vl::grid_blocks(num_reqs, max_q, H, p.block_m, kChunk, p.slots);
+  p.queues = queues && split && !f32;
+  const int64_t upper = num_reqs * H * ((max_q + p.block_m - 1) / p.block_m) + p.slots;
+  const int64_t spare = p.queues ? (upper + 7) / 8 : 0;
+  p.blocks = (num_reqs == 0 || max_q == 0) ? 0
+                                           : vl::grid_blocks(num_reqs, max_q, H, p.block_m, kChunk, p.slots + spare);
   return p;
 }
 
 // Workspace of the split launch: the partial results the key split may
 // write (per slot, BM rows of D floats and BM (offset, sum) float pairs),
-// rounded up to 256 bytes, then V^T ([H][D][vt_ld] bf16).
+// rounded up to 256 bytes; then V^T ([H][D][vt_ld] bf16), rounded up to 256
+// bytes; then 256 bytes holding the kXcds counters of the chiplet queues.
 inline int64_t split_partial_bytes(int slots, int D) {
   return ((int64_t)slots * kBf16VarlenBM * ((int64_t)D * 4 + 8) + 255) / 256 * 256;
 }
+inline int64_t split_vt_bytes(int64_t kv_rows, int64_t num_reqs, int64_t H, int D) {
+  return (H * D * vl::vt_row_len(kv_rows, num_reqs) * 2 + 255) / 256 * 256;
+}
+constexpr int64_t kQueueBytes = 256;
 inline int64_t split_workspace_bytes(int slots, int64_t kv_rows, int64_t num_reqs, int64_t H, int D) {
-  return split_partial_bytes(slots, D) + H * D * vl::vt_row_len(kv_rows, num_reqs) * 2;
+  return split_partial_bytes(slots, D) + split_vt_bytes(kv_rows, num_reqs, H, D) + kQueueBytes;
 }
 
 int launch_status() {
@@ -1769,7 +1851,7 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   // maximum of scale * q.k only for scale > 0 (and a masked score, -inf,
   // times a zero scale would be NaN)
   if (!(scale > 0.f) || std::isinf(scale)) return VL_EINVAL;
-  const VarlenPlan plan = varlen_plan(kF32, split, num_reqs, max_q, max_kv, H, D);
+  const VarlenPlan plan = varlen_plan(kF32, split, split && !noalloc, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
   // the workspace launch stages V^T; its copies address a head's V^T with 32-bit offsets
@@ -1809,6 +1891,8 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   if (stage_vt) {
     a.vt = (char*)workspace + split_partial_bytes(plan.slots, D);
     a.vt_ld = vt_ld;
+    if (plan.queues)
+      a.dyn = (int*)((char*)workspace + split_partial_bytes(plan.slots, D) + split_vt_bytes(kv_rows, num_reqs, H, D));
   }
   (void)hipGetLastError();
   if (kF32) {
@@ -1978,7 +2062,7 @@ int varlen_launch_shape(int32_t max_q, int32_t max_kv, int32_t num_reqs, int32_t
                         int split, int32_t* block_m, int32_t* chunk, int64_t* blocks, int32_t* slots) {
   if (max_q < 0 || max_kv < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
-  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, split != 0, num_reqs, max_q, max_kv, H, D);
+  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, split != 0, split != 0, num_reqs, max_q, max_kv, H, D);
   if (block_m) *block_m = plan.block_m;
   if (chunk) *chunk = kChunk;
   if (blocks) *blocks = plan.blocks;
@@ -1991,7 +2075,7 @@ int varlen_tile_map(const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens, i
                     int64_t max_blocks, vl_stream_t stream) {
   if (max_q < 0 || max_kv < 0 || num_reqs < 0 || H < 1) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
-  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, split != 0, num_reqs, max_q, max_kv, H, D);
+  const VarlenPlan plan = varlen_plan(dtype_f32 != 0, split != 0, split != 0, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G == 0) return VL_OK;
   if (!q_cu_seqlens || !kv_cu_seqlens || !items_out || max_blocks < G) return VL_EINVAL;

@@ -259,7 +259,7 @@ def test_tile_map_bitexact(case, split):
     got = vl.varlen_tile_map(torch.from_numpy(q_cu.astype(np.int32)).to(DEV),
                              torch.from_numpy(kv_cu.astype(np.int32)).to(DEV), max_q, H, D,
                              max_kv=max_kv, split=split).cpu().numpy()
-    ref = oracle.block_schedule(q_cu, kv_cu, H, bm, max_q, chunk, slots=slots, max_kv=max_kv)
+    ref = oracle.block_schedule(q_cu, kv_cu, H, bm, max_q, chunk, slots=slots, max_kv=max_kv, queues=split)
     assert got.shape == ref.shape
     assert np.array_equal(got, ref.astype(np.int32))
     if split and case == "lpt":
@@ -476,6 +476,41 @@ def test_varlen_random_batches(case):
         what = f"random {case} {'f32' if f32 else 'bf16'}{' split' if split else ''}"
         check_close(to64(out), ro, f32, what)
         check_lse(to64(lse), rl, f32, what)
+
+
+# Request lengths of the three full-size workloads' shapes (text + image rows).
+QUEUE_LENS = [[16600], [4196, 7089, 16434, 4182], [32868, 32773, 32968, 32771]]
+
+
+@pytest.mark.parametrize("lens", QUEUE_LENS, ids=["joint", "mixres", "edit"])
+def test_queue_launch_writes_every_row_full_size(lens):
+    """The workspace launch takes its items through the chiplet work queues,
+    so which work-group runs an item changes from call to call.  At full size,
+    three calls into NaN-filled out / lse: every element is written, and
+    equals, bit for bit, the allocation-free launch (static block map, same
+    split plan, V read row-major)."""
+    H, D = 24, 128
+    T = sum(lens)
+    log(f"[queues] lens={lens} T={T}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T)
+    q, k, v = (torch.randn((T, H, D), generator=g, device=DEV).to(torch.bfloat16) for _ in range(3))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=DEV)
+    m = max(lens)
+    scale = wl.softmax_scale(D)
+    ref_out, ref_lse = vl.varlen_attn_fwd_noalloc(q, k, v, cu, cu, m, m, scale, return_lse=True)
+    ws = torch.empty(vl.varlen_split_workspace_bytes(T, len(lens), H, D), dtype=torch.uint8, device=DEV)
+    for rep in range(3):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((T, H), float("nan"), device=DEV)
+        vl.varlen_attn_fwd_split(q, k, v, cu, cu, m, m, scale, out=out, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any().item(), f"call {rep}: rows left unwritten"
+        assert not torch.isnan(lse).any().item(), f"call {rep}: lse left unwritten"
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"call {rep}: out differs"
+        assert torch.equal(lse, ref_lse), f"call {rep}: lse differs"
+    del q, k, v, ws, out, lse, ref_out, ref_lse
+    torch.cuda.empty_cache()
 
 
 SPLIT_CASES = [

@@ -120,7 +120,7 @@ def test_launch_shape_matches_schedule_spec(lib, max_q, R, H, D, split):
     bm, chunk, G, slots = vl.varlen_launch_shape(max_q, R, H, D, max_kv=max_q, split=split)
     if not split:
         assert slots == 0
-    expect = oracle.grid_blocks(R, max_q, H, bm, chunk, slots=slots) if max_q > 0 and R > 0 else 0
+    expect = oracle.grid_blocks(R, max_q, H, bm, chunk, slots=slots, queues=bool(split)) if max_q > 0 and R > 0 else 0
     assert G == expect
     assert G % (8 * chunk) == 0
 
@@ -130,11 +130,13 @@ def test_launch_shape_matches_schedule_spec(lib, max_q, R, H, D, split):
 def test_split_workspace_size_is_the_documented_layout(lib, kv_rows, R, H, D):
     """Partial results of the key split (slots x 256 rows x (D floats + 2
     floats), rounded up to 256 bytes), then V^T: H x D rows of
-    roundup(kv_rows, 64) + 64 R bf16 columns."""
+    roundup(kv_rows, 64) + 64 R bf16 columns, rounded up to 256 bytes, then
+    256 bytes for the counters of the chiplet work queues."""
     _, _, _, slots = vl.varlen_launch_shape(4096, 1, 1, D, max_kv=4096, split=True)
     partial = -(-(slots * 256 * (D * 4 + 8)) // 256) * 256
     vt_ld = -(-kv_rows // 64) * 64 + 64 * R
-    assert vl.varlen_split_workspace_bytes(kv_rows, R, H, D) == partial + H * D * vt_ld * 2
+    vt = -(-(H * D * vt_ld * 2) // 256) * 256
+    assert vl.varlen_split_workspace_bytes(kv_rows, R, H, D) == partial + vt + 256
 
 
 def test_mixfusion_plan_native_matches_oracle_and_pages(lib):

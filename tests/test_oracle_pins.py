@@ -262,6 +262,31 @@ def test_block_schedule_with_split_covers_every_tile_once():
         assert set(split_tiles) == set(tiles[full:])
 
 
+def test_chiplet_queues_partition_the_items_in_block_order():
+    """Every logical item sits in exactly one chiplet queue, and entry k of
+    queue x is the item block_to_logical deals to the k-th block of chiplet x
+    (block 8k + x); queue lengths differ by at most one chunk."""
+    for n_items, chunk in [(0, 32), (1, 32), (255, 32), (256, 32), (1560, 32), (3048, 32), (12480, 32), (77, 5)]:
+        qs = oracle.chiplet_queues(n_items, chunk)
+        assert len(qs) == oracle.XCDS
+        assert sorted(t for q in qs for t in q) == list(range(n_items))
+        for x, q in enumerate(qs):
+            assert q == [oracle.block_to_logical(8 * k + x, chunk) for k in range(len(q))]
+        lens = [len(q) for q in qs]
+        assert max(lens) - min(lens) <= chunk
+
+
+def test_grid_spare_blocks_of_the_queue_launch():
+    """The workspace launch adds an eighth of the item bound in spare blocks,
+    still whole (chiplets x chunk) groups; the static launch does not."""
+    for R, max_q, H, slots in [(1, 16640, 24, 256), (4, 16640, 24, 256), (4, 33024, 24, 256), (3, 210, 2, 0)]:
+        upper = R * H * -(-max_q // 256) + slots
+        g0 = oracle.grid_blocks(R, max_q, H, 256, 32, slots=slots)
+        g1 = oracle.grid_blocks(R, max_q, H, 256, 32, slots=slots, queues=True)
+        assert g0 >= upper and g1 >= upper + -(-upper // 8)
+        assert g0 % 256 == 0 and g1 % 256 == 0 and g1 - 256 < upper + -(-upper // 8) <= g1
+
+
 def test_block_schedule_is_a_bijection_onto_tiles():
     q_cu = oracle.cu_seqlens_from_lengths([17, 64, 129, 300])
     for chunk in (1, 4, 16):
