@@ -519,6 +519,8 @@ SPLIT_CASES = [
     # ragged q tiles, a kv length with empty key ranges, a request with no keys
     ("ragged_empty_parts", [300, 130, 1, 2000], [5000, 70, 0, 2000], 3, 128),
     ("d64_q_ne_kv", [77, 640, 129], [1500, 9, 1300], 2, 64),
+    # more than 64 requests: index order, through the chiplet queues
+    ("many_requests", [int(x) for x in np.random.default_rng(8).integers(0, 700, size=150)], None, 3, 64),
 ]
 
 
