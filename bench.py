@@ -225,8 +225,9 @@ class VarlenStep:
         self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
         self.out_txt = torch.empty_like(self.slabs[0][0])
         self.out_img = torch.empty_like(self.slabs[0][1])
-        # workspace of the attention call (allocated once): staged V^T and the
-        # partial results of the key split of the last round
+        # workspace of the attention call (allocated once): staged V^T, the
+        # partial results of the key split of the last round and the counters
+        # of the chiplet work queues
         self.workspace = torch.empty(vl.varlen_split_workspace_bytes(T, R, H, D), dtype=torch.uint8, device=dev)
         self.pack_items = []
         for (txt, img), dst in zip(self.slabs, self.packed):
