@@ -600,6 +600,7 @@ def main():
         # windows, in the pages' fp32 and in bf16
         prod_n, prod_b = 4000, 2
         detail["block_local_production"] = []
+        detail["block_local_production_memcpy_same_bytes"] = {}
         for pdt in (torch.float32, torch.bfloat16):
             pin = wl.make_block_local_inputs(bl_spec, pdt, n=prod_n, B=prod_b, seed=prod_n)
             pq, pk, pv = pin.q.to(dev), pin.k.to(dev), pin.v.to(dev)
@@ -615,8 +616,12 @@ def main():
                     "us_p90": round(p90, 2), "TFLOP/s": round(fl / med / 1e6, 2),
                     "pct_of_hbm_unique_bytes": round(100 * pbytes / med / 1e3 / HBM_PEAK_GBS, 1)})
             del pq, pk, pv, po, pin
+            detail["block_local_production_memcpy_same_bytes"]["f32" if pdt == torch.float32 else "bf16"] = \
+                memcpy_reference(pbytes, pipelined=False)
         err(f"[bench] block-local production (flushed) us: "
-            f"{[(d['dtype'], d['look_back'], d['look_ahead'], d['us_median']) for d in detail['block_local_production']]}")
+            f"{[(d['dtype'], d['look_back'], d['look_ahead'], d['us_median']) for d in detail['block_local_production']]}"
+            f" (memcpy of the same bytes, flushed: "
+            f"{[(k, m['flushed']['us_median']) for k, m in detail['block_local_production_memcpy_same_bytes'].items()]})")
         # launch floor on this stream: an event pair with nothing between, and
         # one around a one-element kernel
         one_el = torch.zeros(1, device=dev)

@@ -513,6 +513,38 @@ def test_queue_launch_writes_every_row_full_size(lens):
     torch.cuda.empty_cache()
 
 
+def test_queue_launches_on_two_streams_do_not_interfere():
+    """Two workspace launches in flight at once on two streams, each with its
+    own workspace (its own queue counters) and its own batch: each result
+    equals, bit for bit, the same launch run alone."""
+    H, D = 8, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    batches = []
+    for lens in ([3000, 1200, 5000], [700, 4100, 2600, 90]):
+        T = sum(lens)
+        q, k, v = (torch.randn((T, H, D), generator=g, device=DEV).to(torch.bfloat16) for _ in range(3))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=DEV)
+        ws = torch.empty(vl.varlen_split_workspace_bytes(T, len(lens), H, D), dtype=torch.uint8, device=DEV)
+        batches.append((q, k, v, cu, max(lens), ws))
+    scale = wl.softmax_scale(D)
+    alone = []
+    for q, k, v, cu, m, ws in batches:
+        alone.append(vl.varlen_attn_fwd_split(q, k, v, cu, cu, m, m, scale, workspace=ws, return_lse=True))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        outs = []
+        for (q, k, v, cu, m, ws), st in zip(batches, streams):
+            with torch.cuda.stream(st):
+                outs.append(vl.varlen_attn_fwd_split(q, k, v, cu, cu, m, m, scale, workspace=ws, return_lse=True))
+        torch.cuda.synchronize()
+        for (o, l), (o0, l0) in zip(outs, alone):
+            assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), f"round {rep}: out differs"
+            assert torch.equal(l, l0), f"round {rep}: lse differs"
+
+
 SPLIT_CASES = [
     # one round only: every tile is cut
     ("one_request", [3000], None, 2, 128),
