@@ -392,7 +392,7 @@ def main():
     if not args.no_detail:
         flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
-        def call_stats(fn, flushed: bool, reps: int = 30, warm: int = 5):
+        def call_stats(fn, flushed: bool, reps: int = 50, warm: int = 10):
             """median / p10 / p90 of per-call HIP event times (us); all calls are
             enqueued before one synchronisation, so no launch gap is timed;
             flushed: a 512 MB buffer is read before each call, so the 256 MB
