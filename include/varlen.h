@@ -286,10 +286,12 @@ int mixfusion_chunk_plan(const int64_t* token_counts, int32_t n, int64_t min_chu
  *   (request, head, q-tile, part, parts) into items_out[5*b .. 5*b+4]:
  *   part 0 of 1 for a whole tile, key range `part` of `parts` for a split
  *   one, all -1 for an idle work-group; it runs the same device code as the
- *   attention kernel.  For split = 1 it gives the static map, which is also
- *   each chiplet queue's order: the item each work-group takes while every
- *   chiplet keeps to its own queue in work-group order.  items_out: int32 [max_blocks, 5] (device); max_blocks
- *   must be >= the launch size, else VL_EINVAL.
+ *   attention kernel.  For split = 1 it gives the static map; the items it
+ *   assigns to one chiplet's work-groups, in work-group order, are that
+ *   chiplet's queue (which work-group takes which entry then follows the
+ *   order of their tickets).
+ *   items_out: int32 [max_blocks, 5] (device); max_blocks must be >= the
+ *   launch size, else VL_EINVAL.
  *   Schedule: requests by key length descending (ties: lower index first) when
  *   num_reqs <= 64, else in index order; heads ascending; q-tiles ascending.
  *   Work-group b runs on chiplet b mod 8 and takes logical item
