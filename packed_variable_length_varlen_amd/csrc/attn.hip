@@ -100,7 +100,7 @@ struct TileRange {
 constexpr int kStaticItem = -2;
 template <int BM, int BN, bool kBlockLocal>
 __device__ __forceinline__ TileRange tile_range(const AttnArgs& a, int logical_item = kStaticItem) {
-  TileRange t;
+  TileRange t{};
   t.valid = true;
   t.unit = -1;
   if (!kBlockLocal) {
@@ -152,6 +152,51 @@ __device__ __forceinline__ TileRange tile_range(const AttnArgs& a, int logical_i
     t.k_lo = blo * a.block;
     t.k_hi = min(a.n, (bhi + 1) * a.block);
   }
+  return t;
+}
+
+// tile_range's varlen branch for a queue item, on request bounds already in
+// registers (R <= kLptMaxReqs) and the launch's split plan: the same
+// decode with no memory access.  Executed by a whole wave.
+template <int BM, int BN>
+__device__ __forceinline__ TileRange item_range_lanes(const AttnArgs& a, const ReqLanes& rl, const SplitPlan& sp,
+                                                      int logical) {
+  TileRange t{};
+  t.valid = false;
+  t.unit = -1;
+  if (logical < 0) return t;
+  int tile = logical, part = 0, parts = 1, unit = -1;
+  if (sp.parts > 1 && logical >= sp.full) {
+    const int u = logical - sp.full;
+    if (u >= sp.tail * sp.parts) return t;
+    tile = sp.full + u / sp.parts;
+    part = u % sp.parts;
+    parts = sp.parts;
+    unit = u;
+  }
+  int req, head, qt;
+  find_tile_lanes(rl, a.R, a.H, BM, tile, req, head, qt);
+  if (req < 0) return t;
+  const int qs = readlane(rl.qs, req);
+  const int qe = readlane(rl.qe, req);
+  const int ks = readlane(rl.ks, req);
+  const int kv_len = readlane(rl.ke, req) - ks;
+  t.valid = true;
+  t.h = head;
+  t.req = req;
+  t.q0 = qs + qt * BM;
+  t.q1 = min(qe, t.q0 + BM);
+  t.kv_base = ks;
+  t.k_lo = 0;
+  t.k_hi = kv_len;
+  if (unit >= 0) {
+    int lo, hi;
+    split_range((kv_len + BN - 1) / BN, part, parts, lo, hi);
+    t.k_lo = min(kv_len, lo * BN);
+    t.k_hi = min(kv_len, hi * BN);
+    t.unit = unit;
+  }
+  t.seq_q0 = qt * BM;
   return t;
 }
 
@@ -729,27 +774,46 @@ __global__ void __launch_bounds__(512, 1) attn_bf16_pp_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char v1[G::kTileBytes];
   __shared__ __attribute__((aligned(16))) char v2[G::kTileBytes];
 
-  int logical = kStaticItem;
+  // Queue launch: wave 0 takes the ticket, decodes the item once and hands
+  // the tile to the other waves through LDS.  With at most kLptMaxReqs
+  // requests it loads their bounds beside the queue counters, before the
+  // ticket, and decodes from registers; otherwise through tile_range.
+  TileRange tr;
   if (a.dyn != nullptr) {
-    __shared__ int item_s;
+    __shared__ TileRange tr_s;
     if (threadIdx.x < 64) {
       const int x = (int)(blockIdx.x % kXcds);
       int c = 0;
       if (threadIdx.x < kXcds)
         c = __hip_atomic_load(a.dyn + (x + threadIdx.x) % kXcds, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int T = total_tiles(a.q_cu, a.R, a.H, BM);
-      int n_items = T;
-      if (a.slots > 0) {
+      TileRange t0;
+      if (a.R <= kLptMaxReqs) {
+        const ReqLanes rl = load_req_lanes(a.q_cu, a.kv_cu, a.R);
+        const SplitPlan sp = split_plan(total_tiles_lanes(rl, a.R, a.H, BM), a.slots, a.max_kv);
+        const int n_items = sp.parts > 1 ? sp.full + sp.tail * sp.parts : sp.full;
+        t0 = item_range_lanes<BM, BN>(a, rl, sp, take_item(a.dyn, n_items, a.chunk, x, c));
+      } else {
+        const int T = total_tiles(a.q_cu, a.R, a.H, BM);
         const SplitPlan sp = split_plan(T, a.slots, a.max_kv);
-        if (sp.parts > 1) n_items = sp.full + sp.tail * sp.parts;
+        const int n_items = sp.parts > 1 ? sp.full + sp.tail * sp.parts : T;
+        t0 = tile_range<BM, BN, false>(a, take_item(a.dyn, n_items, a.chunk, x, c));
       }
-      const int it = take_item(a.dyn, n_items, a.chunk, x, c);
-      if (threadIdx.x == 0) item_s = it;
+      if (threadIdx.x == 0) tr_s = t0;
     }
     __syncthreads();
-    logical = item_s;
+    tr.valid = tr_s.valid;
+    tr.h = __builtin_amdgcn_readfirstlane(tr_s.h);
+    tr.q0 = __builtin_amdgcn_readfirstlane(tr_s.q0);
+    tr.q1 = __builtin_amdgcn_readfirstlane(tr_s.q1);
+    tr.kv_base = __builtin_amdgcn_readfirstlane(tr_s.kv_base);
+    tr.k_lo = __builtin_amdgcn_readfirstlane(tr_s.k_lo);
+    tr.k_hi = __builtin_amdgcn_readfirstlane(tr_s.k_hi);
+    tr.seq_q0 = __builtin_amdgcn_readfirstlane(tr_s.seq_q0);
+    tr.unit = __builtin_amdgcn_readfirstlane(tr_s.unit);
+    tr.req = __builtin_amdgcn_readfirstlane(tr_s.req);
+  } else {
+    tr = tile_range<BM, BN, false>(a);
   }
-  const TileRange tr = tile_range<BM, BN, false>(a, logical);
   if (!tr.valid) return;
 
   const int tid = threadIdx.x;

@@ -64,6 +64,70 @@ __device__ __forceinline__ int block_to_logical(int b, int chunk) {
   return ((i / chunk) * kXcds + x) * chunk + (i % chunk);
 }
 
+// Bounds of the requests, one request per lane (lane r < R <= kLptMaxReqs):
+// query rows [qs, qe) and key rows [ks, ke); lanes >= R hold zeros.
+struct ReqLanes {
+  int qs, qe, ks, ke;
+};
+__device__ __forceinline__ ReqLanes load_req_lanes(const int32_t* __restrict__ q_cu,
+                                                   const int32_t* __restrict__ kv_cu, int R) {
+  const int lane = lane_id();
+  ReqLanes l{0, 0, 0, 0};
+  if (lane < R) {
+    l.qs = q_cu[lane];
+    l.qe = q_cu[lane + 1];
+    l.ks = kv_cu[lane];
+    l.ke = kv_cu[lane + 1];
+  }
+  return l;
+}
+
+// Number of tiles (see total_tiles) from bounds in registers (R <= kLptMaxReqs).
+__device__ __forceinline__ int total_tiles_lanes(const ReqLanes& l, int R, int H, int block_m) {
+  int cnt = lane_id() < R ? ((l.qe - l.qs + block_m - 1) / block_m) * H : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+  return cnt;
+}
+
+// find_tile (below) for R <= kLptMaxReqs on bounds already in registers:
+// requests by key length descending, ties by lower index.
+__device__ __forceinline__ void find_tile_lanes(const ReqLanes& l, int R, int H, int block_m, int t, int& req,
+                                                int& head, int& qtile) {
+  const int lane = lane_id();
+  req = -1;
+  head = 0;
+  qtile = 0;
+  int kvlen = -1, nt = 0, cnt = 0;
+  if (lane < R) {
+    kvlen = l.ke - l.ks;
+    nt = (l.qe - l.qs + block_m - 1) / block_m;
+    cnt = nt * H;
+  }
+  int rank = 0;
+  for (int s = 0; s < R; ++s) {
+    const int kv_s = readlane(kvlen, s);
+    rank += (kv_s > kvlen) || (kv_s == kvlen && s < lane);
+  }
+  int start = 0;
+  for (int s = 0; s < R; ++s) {
+    const int rank_s = readlane(rank, s);
+    const int cnt_s = readlane(cnt, s);
+    start += (rank_s < rank) ? cnt_s : 0;
+  }
+  const bool hit = lane < R && cnt > 0 && t >= start && t < start + cnt;
+  const uint64_t m = __ballot(hit);
+  if (m) {
+    const int r = __ffsll((unsigned long long)m) - 1;
+    const int st = readlane(start, r);
+    const int ntr = readlane(nt, r);
+    const int local = t - st;
+    req = r;
+    head = local / ntr;
+    qtile = local % ntr;
+  }
+}
+
 // Logical tile t -> (request, head, q-tile) of the varlen schedule; req = -1
 // when t is past the last tile.  Requests are visited by key length
 // descending (ties: lower index first) when R <= kLptMaxReqs, else in index
@@ -77,35 +141,7 @@ __device__ __forceinline__ void find_tile(const int32_t* __restrict__ q_cu,
   head = 0;
   qtile = 0;
   if (R <= kLptMaxReqs) {
-    int kvlen = -1, nt = 0, cnt = 0;
-    if (lane < R) {
-      const int qlen = q_cu[lane + 1] - q_cu[lane];
-      kvlen = kv_cu[lane + 1] - kv_cu[lane];
-      nt = (qlen + block_m - 1) / block_m;
-      cnt = nt * H;
-    }
-    int rank = 0;
-    for (int s = 0; s < R; ++s) {
-      const int kv_s = readlane(kvlen, s);
-      rank += (kv_s > kvlen) || (kv_s == kvlen && s < lane);
-    }
-    int start = 0;
-    for (int s = 0; s < R; ++s) {
-      const int rank_s = readlane(rank, s);
-      const int cnt_s = readlane(cnt, s);
-      start += (rank_s < rank) ? cnt_s : 0;
-    }
-    const bool hit = lane < R && cnt > 0 && t >= start && t < start + cnt;
-    const uint64_t m = __ballot(hit);
-    if (m) {
-      const int r = __ffsll((unsigned long long)m) - 1;
-      const int st = readlane(start, r);
-      const int ntr = readlane(nt, r);
-      const int local = t - st;
-      req = r;
-      head = local / ntr;
-      qtile = local % ntr;
-    }
+    find_tile_lanes(load_req_lanes(q_cu, kv_cu, R), R, H, block_m, t, req, head, qtile);
   } else {
     int base = 0;
     for (int r0 = 0; r0 < R; r0 += 64) {
