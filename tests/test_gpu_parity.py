@@ -553,6 +553,10 @@ SPLIT_CASES = [
     ("d64_q_ne_kv", [77, 640, 129], [1500, 9, 1300], 2, 64),
     # more than 64 requests: index order, through the chiplet queues
     ("many_requests", [int(x) for x in np.random.default_rng(8).integers(0, 700, size=150)], None, 3, 64),
+    # 64 requests, the most whose bounds the queue launch decodes from
+    # registers (one per lane), and 65, decoded through memory
+    ("64_requests", [int(x) for x in np.random.default_rng(9).integers(0, 700, size=64)], None, 2, 64),
+    ("65_requests", [int(x) for x in np.random.default_rng(9).integers(0, 700, size=65)], None, 2, 64),
 ]
 
 
