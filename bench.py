@@ -2,9 +2,11 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   1. boundaries (cu_seqlens) from the real text mask and the image grids,
-  2. joint text+image pack of Q, K and V into flat [T, H, D] (one launch),
-  3. flat varlen attention (bf16 MFMA, fp32 accumulation; the last, partial
-     round of work-groups cut along the keys and merged),
+  2. joint text+image pack of Q and K into flat [T, H, D] (one launch) and of
+     V straight into the transposed layout the attention kernel reads (V^T in
+     the attention call's workspace; the pack and the V^T staging in one pass),
+  3. flat varlen attention on that V^T (bf16 MFMA, fp32 accumulation; the
+     last, partial round of work-groups cut along the keys and merged),
   4. unpack of the output back to the per-request text / image layout (one
      launch),
   5. block-local attention of the vocoder-DiT shape (n=2003, 24-frame blocks,
@@ -21,7 +23,8 @@ value = algorithmic FLOP of one step / step time, where the FLOP count is
 block-local pairs); work the kernels avoid is never counted.
 
 The `detail` object holds the same step at the two other full-size workloads,
-the bandwidth-bound pieces alone (warm and with the last-level cache flushed),
+the bandwidth-bound pieces alone (the flat pack of all six Q/K/V pieces and the
+unpack; warm and with the last-level cache flushed),
 each beside the runtime's own device-to-device memcpy of the same bytes timed
 the same way (the practical ceiling at that size), the block-local calls per window and weighted by the DiT's layer mix, the
 production block-local shape, the fused CFG combine, and the launch floor.
@@ -225,13 +228,17 @@ class VarlenStep:
         self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
         self.out_txt = torch.empty_like(self.slabs[0][0])
         self.out_img = torch.empty_like(self.slabs[0][1])
-        # workspace of the attention call (allocated once): staged V^T, the
-        # partial results of the key split of the last round and the counters
-        # of the chiplet work queues
+        # workspace of the attention call (allocated once): V^T (packed there
+        # straight from the V pieces), the partial results of the key split of
+        # the last round and the counters of the chiplet work queues
         self.workspace = torch.empty(vl.varlen_split_workspace_bytes(T, R, H, D), dtype=torch.uint8, device=dev)
+        # the flat pack of all six pieces (the pack primitive, timed alone) ...
         self.pack_items = []
         for (txt, img), dst in zip(self.slabs, self.packed):
             self.pack_items += [(txt, self.cu_t, dst, self.cu_j[:-1]), (img, self.cu_i, dst, self.img_dst)]
+        # ... and the step's: Q and K flat, V straight into V^T
+        self.pack_qk_items = self.pack_items[:4]
+        self.pack_v_items = [(self.slabs[2][0], self.cu_t, self.cu_j[:-1]), (self.slabs[2][1], self.cu_i, self.img_dst)]
         self.unpack_items = [(self.out, self.cu_t, self.out_txt, self.cu_j[:-1]),
                              (self.out, self.cu_i, self.out_img, self.img_dst)]
         row_bytes = H * D * 2
@@ -242,13 +249,17 @@ class VarlenStep:
     def cu(self):
         self.vl.joint_cu_seqlens(self.mask_d, self.hw_d, outs=(self.cu_j, self.cu_t, self.cu_i, self.img_dst))
 
-    def pack(self):
+    def pack_flat(self):
         self.vl.pack_by_cu_seqlens_batched(self.pack_items)
 
+    def pack(self):
+        self.vl.pack_by_cu_seqlens_batched(self.pack_qk_items)
+        self.vl.pack_v_transposed(self.pack_v_items, self.cu_j, self.T, self.workspace)
+
     def attention(self):
-        q, k, v = self.packed
-        self.vl.varlen_attn_fwd_split(q, k, v, self.cu_j, self.cu_j, self.max_len, self.max_len, self.inp.scale,
-                                      out=self.out, workspace=self.workspace)
+        q, k, _ = self.packed
+        self.vl.varlen_attn_fwd_vt(q, k, self.cu_j, self.cu_j, self.max_len, self.max_len, self.workspace,
+                                   self.inp.scale, out=self.out)
 
     def unpack(self):
         self.vl.unpack_by_cu_seqlens_batched(self.unpack_items)
@@ -483,7 +494,7 @@ def main():
                 uitems = [(out, s.cu_t, torch.empty_like(s.out_txt), s.cu_j[:-1]),
                           (out, s.cu_i, torch.empty_like(s.out_img), s.img_dst)]
                 extra.append((pitems, uitems))
-            for what, fn, nbytes in (("pack", s.pack, s.pack_bytes), ("unpack", s.unpack, s.unpack_bytes)):
+            for what, fn, nbytes in (("pack", s.pack_flat, s.pack_bytes), ("unpack", s.unpack, s.unpack_bytes)):
                 rec = {"workload": s.inp.spec.name, "copy": what, **bw_record(nbytes, fn)}
                 k = 0 if what == "pack" else 1
                 call = vl.pack_by_cu_seqlens_batched if what == "pack" else vl.unpack_by_cu_seqlens_batched
@@ -665,8 +676,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "vt_transpose_kernel<128> + attn_bf16_pp_kernel<128, 64, true> + "
-                      "split_merge_kernel<128, 256> (varlen_attn_fwd_split)",
+            "kernel": "zero_counters_kernel + attn_bf16_pp_kernel<128, 64, true> + "
+                      "split_merge_kernel<128, 256> (varlen_attn_fwd_vt)",
             "kernel_ms": round(attn_ms, 4),
             "algorithmic_flop_per_launch": flop_varlen,
         },

@@ -214,6 +214,42 @@ int varlen_attn_fwd_split(const void* q, const void* k, const void* v, const int
                           void* workspace, int64_t workspace_bytes, vl_stream_t stream);
 int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, int32_t D, int64_t* bytes);
 
+/* pack_v_transposed + varlen_attn_fwd_vt: the pack of V and the V^T staging
+ *   of varlen_attn_fwd_split in one pass (PR #4024 "How batching works":
+ *   only real tokens are packed; PR #6711 "Key changes": K/V of all
+ *   requests concatenated with kv_cu_seqlens as their boundaries), so V is
+ *   read from its padded buffers and written once, straight in the layout
+ *   the attention kernel reads.
+ * pack_v_transposed: descs[i] (HOST array, read during the call) names piece
+ *   i of V as pack_by_cu_seqlens would copy it: rows [0, len_r) of
+ *   src + r * max_len rows (len_r = cu_seqlens[r+1] - cu_seqlens[r]) are
+ *   the flat key rows row_offsets[r] (NULL => cu_seqlens[r]) onward; dst and
+ *   zero_fill are ignored.  Every descriptor must have num_reqs requests and
+ *   row_bytes = H * D * 2 (bf16 rows of H heads of D features) and a 16-byte
+ *   aligned src; 1 <= count <= 8.  Instead of flat rows the call writes V^T
+ *   into `workspace` (as varlen_attn_fwd_split stages it): request r's keys
+ *   kv_cu_seqlens[r] .. kv_cu_seqlens[r+1]-1 take their rows from the piece
+ *   that covers them (the first one, where pieces overlap), a key no piece
+ *   covers reads as zero, and the columns past each request's last key up
+ *   to its next multiple of 64 are zero.  kv_rows, num_reqs, H, D,
+ *   workspace, workspace_bytes: as for varlen_attn_fwd_split; len_r <=
+ *   max_len is trusted.
+ * varlen_attn_fwd_vt: varlen_attn_fwd_split on q, k and the V^T that
+ *   pack_v_transposed left in `workspace` (same kv_cu_seqlens, num_reqs, H,
+ *   D and kv_rows); out and lse are the same bits as varlen_attn_fwd_split's
+ *   on the V those pieces pack.  The V^T is only read, so the call may be
+ *   repeated on one staging; it clears the queue counters itself.
+ *   Both: the V^T starts after room for the partial results of every
+ *   resident work-group (the size varlen_split_workspace_bytes reports),
+ *   whatever max_kv is; a workspace shorter than that returns VL_EINVAL.
+ */
+int pack_v_transposed(const vl_copy_desc* descs, int32_t count, const int32_t* kv_cu_seqlens, int32_t num_reqs,
+                      int32_t H, int32_t D, int64_t kv_rows, void* workspace, int64_t workspace_bytes,
+                      vl_stream_t stream);
+int varlen_attn_fwd_vt(const void* q, const void* k, const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens,
+                       int32_t max_q, int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale, void* out,
+                       float* lse, int64_t kv_rows, void* workspace, int64_t workspace_bytes, vl_stream_t stream);
+
 /* varlen_attn_fwd_noalloc: for callers that cannot allocate device memory
  *   (code under HIP graph capture, tight serving loops, harnesses that forbid
  *   hipMalloc).  Same arguments and contract as varlen_attn_fwd; it runs the

@@ -20,7 +20,7 @@ __all__ = [
     "pack_by_cu_seqlens", "unpack_by_cu_seqlens", "pack_by_cu_seqlens_batched",
     "unpack_by_cu_seqlens_batched", "varlen_attn_fwd", "varlen_attn_fwd_split",
     "varlen_split_workspace_bytes", "varlen_attn_fwd_f32", "varlen_attn_fwd_noalloc",
-    "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
+    "pack_v_transposed", "varlen_attn_fwd_vt", "block_local_attn_fwd", "block_local_attn_fwd_f32", "varlen_launch_shape", "varlen_tile_map",
     "mixfusion_chunk_plan", "unpack_cfg_combine", "VarlenError", "validate_cu_seqlens",
 ]
 
@@ -52,6 +52,9 @@ _SIGNATURES = {
     "varlen_attn_fwd_split": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                _vp, _vp, _c_i64, _vp, _c_i64, _vp], _c_int),
     "varlen_split_workspace_bytes": ([_c_i64, _c_i32, _c_i32, _c_i32, _vp], _c_int),
+    "pack_v_transposed": ([_vp, _c_i32, _vp, _c_i32, _c_i32, _c_i32, _c_i64, _vp, _c_i64, _vp], _c_int),
+    "varlen_attn_fwd_vt": ([_vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64,
+                            _vp, _c_i64, _vp], _c_int),
     "varlen_attn_fwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                  _vp, _vp, _vp], _c_int),
     "varlen_launch_shape": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_int, _c_int, _vp, _vp, _vp, _vp],
@@ -313,7 +316,8 @@ def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse
         raise VarlenError("the flat varlen path takes no attention mask")
     if padded_tokens != 0:
         raise VarlenError("the flat varlen path requires padded_tokens == 0")
-    _attn_prep(q, k, v, dtype)
+    staged = fn_name == "varlen_attn_fwd_vt"  # V comes as the V^T staged in the workspace
+    _attn_prep(q, k, k if staged else v, dtype)
     if q.dim() != 3:
         raise VarlenError("q, k, v must be packed [total_tokens, heads, head_dim]")
     _gpu(q_cu, "q_cu_seqlens", torch.int32)
@@ -340,7 +344,13 @@ def _varlen(fn_name, dtype, q, k, v, q_cu, kv_cu, max_q, max_kv, scale, out, lse
             raise VarlenError("lse must be [total_tokens, heads]")
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(q_cu), _ptr(kv_cu), int(max_q), int(max_kv), R, H, D, float(scale),
             _ptr(out), _ptr(lse)]
-    if fn_name == "varlen_attn_fwd_split":
+    if staged:
+        if workspace is None:
+            raise VarlenError("varlen_attn_fwd_vt reads the V^T that pack_v_transposed staged in its workspace")
+        _gpu(workspace, "workspace")
+        args = [_ptr(q), _ptr(k), _ptr(q_cu), _ptr(kv_cu), int(max_q), int(max_kv), R, H, D, float(scale),
+                _ptr(out), _ptr(lse), k.shape[0], _ptr(workspace), workspace.numel() * workspace.element_size()]
+    elif fn_name == "varlen_attn_fwd_split":
         kv_rows = k.shape[0]
         need = varlen_split_workspace_bytes(kv_rows, R, H, D)
         if workspace is None:
@@ -385,6 +395,51 @@ def varlen_attn_fwd_split(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, s
     is allocated when not given."""
     return _varlen("varlen_attn_fwd_split", torch.bfloat16, q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q,
                    max_kv, scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace,
+                   check_cu_seqlens=check_cu_seqlens)
+
+
+def pack_v_transposed(items, kv_cu_seqlens, kv_rows: int, workspace, stream=None):
+    """V packed from its padded buffers straight into the V^T staging of the
+    workspace launch (the pack and the staging in one pass).  items: 1 to 8
+    tuples (src_padded [num_reqs, max_len, H, D] bf16, cu_seqlens,
+    flat_row_offsets or None), the pieces of V as pack_by_cu_seqlens_batched
+    would copy them into the flat [kv_rows, H, D] tensor; kv_cu_seqlens: the
+    requests' key boundaries in that flat numbering; workspace: at least
+    varlen_split_workspace_bytes(kv_rows, num_reqs, H, D) bytes, then given
+    to varlen_attn_fwd_vt."""
+    items = list(items)
+    if not 1 <= len(items) <= MAX_BATCH:
+        raise VarlenError(f"1 to {MAX_BATCH} pieces per call")
+    _gpu(kv_cu_seqlens, "kv_cu_seqlens", torch.int32)
+    _gpu(workspace, "workspace")
+    R = kv_cu_seqlens.numel() - 1
+    row = None
+    descs = (_CopyDesc * len(items))()
+    for i, (src, cu, offs) in enumerate(items):
+        _gpu(src, "src_padded", torch.bfloat16)
+        _gpu(cu, "cu_seqlens", torch.int32)
+        if offs is not None:
+            _gpu(offs, "flat_row_offsets", torch.int32)
+        if src.dim() != 4 or src.shape[0] != R or cu.numel() != R + 1:
+            raise VarlenError("src_padded must be [num_reqs, max_len, H, D] and cu_seqlens [num_reqs + 1]")
+        if row is not None and tuple(src.shape[2:]) != row:
+            raise VarlenError("every piece must have the same H and D")
+        row = tuple(src.shape[2:])
+        descs[i] = _CopyDesc(_ptr(src), None, _ptr(cu), _ptr(offs), src.shape[1], row[0] * row[1] * 2, R, 0)
+    H, D = row
+    _check(load_library().pack_v_transposed(ctypes.cast(descs, _vp), len(items), _ptr(kv_cu_seqlens), R, H, D,
+                                            int(kv_rows), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream)),
+           "pack_v_transposed")
+
+
+def varlen_attn_fwd_vt(q, k, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, workspace, scale=None, out=None, lse=None,
+                       padded_tokens: int = 0, attn_mask=None, return_lse: bool = False, stream=None,
+                       check_cu_seqlens: bool = False):
+    """varlen_attn_fwd_split with V taken from the V^T that pack_v_transposed
+    staged in `workspace` (same kv_cu_seqlens; kv_rows = k.shape[0])."""
+    return _varlen("varlen_attn_fwd_vt", torch.bfloat16, q, k, None, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv,
+                   scale, out, lse, padded_tokens, attn_mask, return_lse, stream, workspace,
                    check_cu_seqlens=check_cu_seqlens)
 
 

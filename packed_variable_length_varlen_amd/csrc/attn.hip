@@ -1644,45 +1644,50 @@ __global__ void __launch_bounds__(64 * kBlockWaves, 3) block_local_bf16_kernel(A
 
 // ---------------------------------------------------------------- V^T staging
 
-// One 64-key tile of one head of V -> V^T: V rows [T, H, D] (bf16) of request
-// r's keys key0 .. key0+63 become D rows of 64 columns at
+// One 64-key tile of one head of V -> V^T: the V rows (bf16) of request r's
+// keys key0 .. key0+63 become D rows of 64 columns at
 // vt_col_base(kv_cu[r], r) + key0, each 16-key group stored in the P k-slot
 // order (vt_pos_of_key), keys past the request zero.  Block b covers column
 // tile b mod (vt_ld / 64) of head b / (vt_ld / 64); tiles in the gaps between
 // requests are never read and are skipped.  Through LDS so that both the V
 // reads (16 lanes per 256-byte row) and the V^T writes (8 lanes per 128-byte
-// row) are whole-line accesses.
-template <int D>
-__global__ void __launch_bounds__(256) vt_transpose_kernel(AttnArgs a) {
+// row) are whole-line accesses.  The rows come from `src`: src.prepare(r) is
+// called by every thread once the tile's request r is known (it may use
+// __syncthreads), then src.row(f, h) gives head h of flat key row f of the
+// request, or nullptr for a row that reads as zero.
+template <int D, typename Src>
+__device__ __forceinline__ void vt_tile(const int32_t* __restrict__ kv_cu, int R, int H, __bf16* vt, int64_t vt_ld,
+                                        Src& src) {
   constexpr int LD = D + 2;  // bf16 per LDS row: an odd dword count, so column reads spread over banks
   constexpr int CPR = D / 8;
   __shared__ uint32_t sm[kVtTile * LD / 2];
-  // the attention kernel that follows starts its chiplet queues from zero
-  if (a.dyn != nullptr && blockIdx.x == 0 && threadIdx.x < kXcds) a.dyn[threadIdx.x] = 0;
-  const int ntc = (int)(a.vt_ld / kVtTile);
+  const int ntc = (int)(vt_ld / kVtTile);
   const int h = blockIdx.x / ntc;
   const int64_t col0 = (int64_t)(blockIdx.x % ntc) * kVtTile;
   // request of the tile: the last r whose first column is <= col0
-  int lo = 0, hi = a.R - 1;
+  int lo = 0, hi = R - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (vt_col_base(a.kv_cu[mid], mid) <= col0)
+    if (vt_col_base(kv_cu[mid], mid) <= col0)
       lo = mid;
     else
       hi = mid - 1;
   }
-  const int kv0 = a.kv_cu[lo];
-  const int len = a.kv_cu[lo + 1] - kv0;
+  const int kv0 = kv_cu[lo];
+  const int len = kv_cu[lo + 1] - kv0;
   const int64_t key0 = col0 - vt_col_base(kv0, lo);
   if (key0 < 0 || key0 >= len) return;
+  src.prepare(lo);
   const int valid = min(kVtTile, len - (int)key0);
   const int t = threadIdx.x;
 #pragma unroll
   for (int i = t; i < kVtTile * CPR; i += 256) {
     const int k = i / CPR, ch = i % CPR;
     uint4 x = make_uint4(0u, 0u, 0u, 0u);
-    if (k < valid)
-      x = *(const uint4*)((const __bf16*)a.v + ((int64_t)(kv0 + key0 + k) * a.H + h) * D + ch * 8);
+    if (k < valid) {
+      const __bf16* row = src.row(kv0 + (int)key0 + k, h);
+      if (row != nullptr) x = *(const uint4*)(row + ch * 8);
+    }
     uint32_t* d = sm + (k * LD + ch * 8) / 2;
     d[0] = x.x;
     d[1] = x.y;
@@ -1704,8 +1709,87 @@ __global__ void __launch_bounds__(256) vt_transpose_kernel(AttnArgs a) {
       const int k1 = base + 4 * (p1 >> 3) + (p1 & 3) + 8 * ((p1 >> 2) & 1);
       w[j / 2] = (uint32_t)sh[k0 * LD + d] | ((uint32_t)sh[k1 * LD + d] << 16);
     }
-    *(uint4*)((__bf16*)a.vt + ((int64_t)h * D + d) * a.vt_ld + col0 + cc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(vt + ((int64_t)h * D + d) * vt_ld + col0 + cc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+// V rows of the packed [T, H, D] tensor.
+template <int D>
+struct FlatVRows {
+  const __bf16* v;
+  int H;
+  __device__ void prepare(int) {}
+  __device__ const __bf16* row(int f, int h) const { return v + ((int64_t)f * H + h) * D; }
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) vt_transpose_kernel(AttnArgs a) {
+  // the attention kernel that follows starts its chiplet queues from zero
+  if (a.dyn != nullptr && blockIdx.x == 0 && threadIdx.x < kXcds) a.dyn[threadIdx.x] = 0;
+  FlatVRows<D> src{(const __bf16*)a.v, a.H};
+  vt_tile<D>(a.kv_cu, a.R, a.H, (__bf16*)a.vt, a.vt_ld, src);
+}
+
+// V packed straight from padded per-request buffers into V^T (the pack and
+// the staging in one pass).  Piece p of request r is the rows
+// [0, cu[r+1] - cu[r]) of src + r * max_len rows, which are flat key rows
+// off[r] (cu[r] when off is null) onward of the request's packed numbering.
+constexpr int kMaxVtPieces = 8;
+struct VtPiece {
+  const void* src;
+  const int32_t* cu;
+  const int32_t* off;
+  int64_t max_len;
+};
+struct PackVtArgs {
+  VtPiece piece[kMaxVtPieces];
+  int count;
+  const int32_t* kv_cu;
+  int R;
+  int H;
+  void* vt;
+  int64_t vt_ld;
+};
+
+// Rows of the pieces: prepare(r) puts each piece's first flat row and length
+// for request r in LDS; a key row no piece covers reads as zero.
+template <int D>
+struct PieceVRows {
+  const PackVtArgs* p;
+  int r;
+  int* s_off;
+  int* s_len;
+  __device__ void prepare(int req) {
+    r = req;
+    const int t = threadIdx.x;
+    if (t < p->count) {
+      const VtPiece& pc = p->piece[t];
+      s_off[t] = pc.off != nullptr ? pc.off[req] : pc.cu[req];
+      s_len[t] = pc.cu[req + 1] - pc.cu[req];
+    }
+    __syncthreads();
+  }
+  __device__ const __bf16* row(int f, int h) const {
+    for (int i = 0; i < p->count; ++i) {
+      const int d = f - s_off[i];
+      if (d >= 0 && d < s_len[i])
+        return (const __bf16*)p->piece[i].src + (((int64_t)r * p->piece[i].max_len + d) * p->H + h) * D;
+    }
+    return nullptr;
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) pack_vt_kernel(PackVtArgs a) {
+  __shared__ int s_off[kMaxVtPieces], s_len[kMaxVtPieces];
+  PieceVRows<D> src{&a, 0, s_off, s_len};
+  vt_tile<D>(a.kv_cu, a.R, a.H, (__bf16*)a.vt, a.vt_ld, src);
+}
+
+// Zeroes the chiplet-queue counters before an attention launch that reads a
+// V^T staged by an earlier call.
+__global__ void __launch_bounds__(64) zero_counters_kernel(int* cnt) {
+  if (threadIdx.x < kXcds) cnt[threadIdx.x] = 0;
 }
 
 // ---------------------------------------------------------------- split merge
@@ -1870,6 +1954,11 @@ inline int64_t split_workspace_bytes(int slots, int64_t kv_rows, int64_t num_req
   return split_partial_bytes(slots, D) + split_vt_bytes(kv_rows, num_reqs, H, D) + kQueueBytes;
 }
 
+// Where a V^T staged by pack_v_transposed starts in the workspace: after the
+// partial results of every resident work-group, whatever max_kv is, so that
+// the pack and the attention call that reads it agree without sharing max_kv.
+inline int64_t staged_vt_offset(int D) { return split_partial_bytes(bf16_varlen_slots(D), D); }
+
 int launch_status() {
   return hipGetLastError() == hipSuccess ? VL_OK : VL_ELAUNCH;
 }
@@ -1905,12 +1994,13 @@ template <bool kF32>
 int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_cu,
                   const int32_t* kv_cu, int32_t max_q, int32_t max_kv, int32_t num_reqs,
                   int32_t H, int32_t D, float scale, void* out, float* lse, bool split, int64_t kv_rows,
-                  void* workspace, int64_t workspace_bytes, hipStream_t stream, bool noalloc = false) {
+                  void* workspace, int64_t workspace_bytes, hipStream_t stream, bool noalloc = false,
+                  bool staged_vt = false) {
   if (num_reqs < 0 || max_q < 0 || max_kv < 0 || H < 1 || kv_rows < 0) return VL_EINVAL;
   if (D != 64 && D != 128) return VL_EUNSUPPORTED;
   if (num_reqs == 0 || max_q == 0) return VL_OK;
-  if (!q || !k || !v || !q_cu || !kv_cu || !out) return VL_EINVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return VL_EINVAL;
+  if (!q || !k || (!v && !staged_vt) || !q_cu || !kv_cu || !out) return VL_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(out)) return VL_EINVAL;
   // the online softmax tracks the maximum of the raw scores: that is the
   // maximum of scale * q.k only for scale > 0 (and a masked score, -inf,
   // times a zero scale would be NaN)
@@ -1918,13 +2008,17 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   const VarlenPlan plan = varlen_plan(kF32, split, split && !noalloc, num_reqs, max_q, max_kv, H, D);
   const int64_t G = plan.blocks;
   if (G > INT32_MAX) return VL_EUNSUPPORTED;
-  // the workspace launch stages V^T; its copies address a head's V^T with 32-bit offsets
-  const bool stage_vt = split && !noalloc;
-  const int64_t vt_ld = stage_vt ? vl::vt_row_len(kv_rows, num_reqs) : 0;
-  if (stage_vt && ((int64_t)D * vt_ld * 2 > INT32_MAX || vt_ld / vl::kVtTile * H > INT32_MAX))
+  // the workspace launch stages V^T (or, staged_vt, reads the one
+  // pack_v_transposed staged); its copies address a head's V^T with 32-bit offsets
+  const bool use_vt = split && !noalloc;
+  const bool stage_vt = use_vt && !staged_vt;
+  const int64_t vt_ld = use_vt ? vl::vt_row_len(kv_rows, num_reqs) : 0;
+  if (use_vt && ((int64_t)D * vt_ld * 2 > INT32_MAX || vt_ld / vl::kVtTile * H > INT32_MAX))
     return VL_EUNSUPPORTED;
-  if (stage_vt && (!workspace || !aligned16(workspace) ||
-                   workspace_bytes < split_workspace_bytes(plan.slots, kv_rows, num_reqs, H, D)))
+  const int64_t vt_off = staged_vt ? staged_vt_offset(D) : split_partial_bytes(plan.slots, D);
+  if (use_vt &&
+      (!workspace || !aligned16(workspace) ||
+       workspace_bytes < vt_off + split_vt_bytes(kv_rows, num_reqs, H, D) + kQueueBytes))
     return VL_EINVAL;
   if (noalloc) {
     // the partials must fit the static scratch; its address is this device's
@@ -1952,11 +2046,10 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
   a.slots = plan.slots;
   a.max_kv = max_kv;
   a.ws = (float*)workspace;
-  if (stage_vt) {
-    a.vt = (char*)workspace + split_partial_bytes(plan.slots, D);
+  if (use_vt) {
+    a.vt = (char*)workspace + vt_off;
     a.vt_ld = vt_ld;
-    if (plan.queues)
-      a.dyn = (int*)((char*)workspace + split_partial_bytes(plan.slots, D) + split_vt_bytes(kv_rows, num_reqs, H, D));
+    if (plan.queues) a.dyn = (int*)((char*)workspace + vt_off + split_vt_bytes(kv_rows, num_reqs, H, D));
   }
   (void)hipGetLastError();
   if (kF32) {
@@ -1966,17 +2059,22 @@ int varlen_common(const void* q, const void* k, const void* v, const int32_t* q_
       hipLaunchKernelGGL((vl::attn_f32_kernel<64, false>), dim3((unsigned)G), dim3(plan.threads), 0, stream, a);
     return launch_status();
   }
-  if (stage_vt) {
+  if (use_vt) {
     const unsigned tb = (unsigned)(vt_ld / vl::kVtTile * H);
-    if (D == 128) {
-      hipLaunchKernelGGL((vl::vt_transpose_kernel<128>), dim3(tb), dim3(256), 0, stream, a);
+    if (stage_vt) {
+      if (D == 128)
+        hipLaunchKernelGGL((vl::vt_transpose_kernel<128>), dim3(tb), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((vl::vt_transpose_kernel<64>), dim3(tb), dim3(256), 0, stream, a);
+    } else if (a.dyn != nullptr) {
+      hipLaunchKernelGGL(vl::zero_counters_kernel, dim3(1), dim3(64), 0, stream, a.dyn);
+    }
+    if (D == 128)
       hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<128, kBf16VarlenBN, true>), dim3((unsigned)G),
                          dim3(plan.threads), 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((vl::vt_transpose_kernel<64>), dim3(tb), dim3(256), 0, stream, a);
+    else
       hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<64, kBf16VarlenBN, true>), dim3((unsigned)G),
                          dim3(plan.threads), 0, stream, a);
-    }
   } else if (D == 128) {
     hipLaunchKernelGGL((vl::attn_bf16_pp_kernel<128, kBf16VarlenBN, false>), dim3((unsigned)G), dim3(plan.threads),
                        0, stream, a);
@@ -2089,6 +2187,48 @@ int varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, const i
                             int32_t H, int32_t D, float scale, void* out, float* lse, vl_stream_t stream) {
   return varlen_common<false>(q, k, v, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D,
                               scale, out, lse, true, 0, nullptr, 0, (hipStream_t)stream, true);
+}
+
+int pack_v_transposed(const vl_copy_desc* descs, int32_t count, const int32_t* kv_cu_seqlens, int32_t num_reqs,
+                      int32_t H, int32_t D, int64_t kv_rows, void* workspace, int64_t workspace_bytes,
+                      vl_stream_t stream) {
+  if (num_reqs < 0 || H < 1 || kv_rows < 0 || count < 1 || count > vl::kMaxVtPieces || !descs) return VL_EINVAL;
+  if (D != 64 && D != 128) return VL_EUNSUPPORTED;
+  vl::PackVtArgs a{};
+  for (int i = 0; i < count; ++i) {
+    const vl_copy_desc& d = descs[i];
+    if (!d.src || !d.cu_seqlens || !aligned16(d.src) || d.max_len < 0 || d.num_reqs != num_reqs ||
+        d.row_bytes != (int64_t)H * D * 2)
+      return VL_EINVAL;
+    a.piece[i] = vl::VtPiece{d.src, d.cu_seqlens, d.row_offsets, d.max_len};
+  }
+  if (num_reqs == 0) return VL_OK;
+  const int64_t vt_ld = vl::vt_row_len(kv_rows, num_reqs);
+  if ((int64_t)D * vt_ld * 2 > INT32_MAX || vt_ld / vl::kVtTile * H > INT32_MAX) return VL_EUNSUPPORTED;
+  const int64_t vt_off = staged_vt_offset(D);
+  if (!kv_cu_seqlens || !workspace || !aligned16(workspace) ||
+      workspace_bytes < vt_off + split_vt_bytes(kv_rows, num_reqs, H, D) + kQueueBytes)
+    return VL_EINVAL;
+  a.count = count;
+  a.kv_cu = kv_cu_seqlens;
+  a.R = num_reqs;
+  a.H = H;
+  a.vt = (char*)workspace + vt_off;
+  a.vt_ld = vt_ld;
+  (void)hipGetLastError();
+  const unsigned tb = (unsigned)(vt_ld / vl::kVtTile * H);
+  if (D == 128)
+    hipLaunchKernelGGL((vl::pack_vt_kernel<128>), dim3(tb), dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((vl::pack_vt_kernel<64>), dim3(tb), dim3(256), 0, (hipStream_t)stream, a);
+  return launch_status();
+}
+
+int varlen_attn_fwd_vt(const void* q, const void* k, const int32_t* q_cu_seqlens, const int32_t* kv_cu_seqlens,
+                       int32_t max_q, int32_t max_kv, int32_t num_reqs, int32_t H, int32_t D, float scale, void* out,
+                       float* lse, int64_t kv_rows, void* workspace, int64_t workspace_bytes, vl_stream_t stream) {
+  return varlen_common<false>(q, k, nullptr, q_cu_seqlens, kv_cu_seqlens, max_q, max_kv, num_reqs, H, D, scale,
+                              out, lse, true, kv_rows, workspace, workspace_bytes, (hipStream_t)stream, false, true);
 }
 
 int varlen_split_workspace_bytes(int64_t kv_rows, int32_t num_reqs, int32_t H, int32_t D, int64_t* bytes) {

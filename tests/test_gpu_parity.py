@@ -513,6 +513,81 @@ def test_queue_launch_writes_every_row_full_size(lens):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_packed_vt_pieces_and_gaps_vs_oracle(D):
+    """V packed from two padded pieces straight into V^T (pack_v_transposed)
+    and attended through it (varlen_attn_fwd_vt), q != kv: keys no piece
+    covers read as zero V (a gap inside request 0, a trailing gap in request
+    2), a request without keys gives 0 / -inf.  Against the oracle on the V
+    those pieces pack, and bit for bit against varlen_attn_fwd_split on the
+    same V packed flat."""
+    H = 2
+    kl = [70, 1, 700, 0]
+    ql = [33, 5, 130, 7]
+    a_len = [30, 0, 600, 0]     # piece A: the first rows of each request
+    gap = [10, 0, 100, 0]       # then rows no piece covers
+    b_len = [kl[r] - a_len[r] - gap[r] for r in range(4)]  # piece B: the rest
+    R = len(kl)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    q_cu = oracle.cu_seqlens_from_lengths(ql)
+    rng = np.random.default_rng(D + 5)
+    bf = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    q, k = bf(int(q_cu[-1]), H, D), bf(int(kv_cu[-1]), H, D)
+    slab_a, slab_b = bf(R, max(a_len), H, D), bf(R, max(b_len), H, D)
+    v_flat = torch.zeros((int(kv_cu[-1]), H, D), dtype=torch.bfloat16)
+    for r in range(R):
+        v_flat[kv_cu[r]:kv_cu[r] + a_len[r]] = slab_a[r, :a_len[r]]
+        o = kv_cu[r] + a_len[r] + gap[r]
+        v_flat[o:o + b_len[r]] = slab_b[r, :b_len[r]]
+    scale = wl.softmax_scale(D)
+    ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v_flat), q_cu, kv_cu, scale)
+    ref_out, ref_lse = _run_varlen(q, k, v_flat, q_cu, kv_cu, scale, False, split=True)
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32), device=DEV)
+    T = int(kv_cu[-1])
+    ws = torch.full((vl.varlen_split_workspace_bytes(T, R, H, D),), 0xFF, dtype=torch.uint8, device=DEV)
+    vl.pack_v_transposed([(slab_a.to(DEV), i32(oracle.cu_seqlens_from_lengths(a_len)), i32(kv_cu[:-1])),
+                          (slab_b.to(DEV), i32(oracle.cu_seqlens_from_lengths(b_len)),
+                           i32(np.asarray(kv_cu[:-1]) + np.asarray(a_len) + np.asarray(gap)))],
+                         i32(kv_cu), T, ws)
+    for rep in range(2):
+        out = torch.full((int(q_cu[-1]), H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((int(q_cu[-1]), H), float("nan"), device=DEV)
+        vl.varlen_attn_fwd_vt(q.to(DEV), k.to(DEV), i32(q_cu), i32(kv_cu), max(ql), max(kl), ws, scale,
+                              out=out, lse=lse)
+        torch.cuda.synchronize()
+        check_close(to64(out), ro, False, f"packed V^T D={D} call {rep}")
+        check_lse(to64(lse), rl, False, f"packed V^T D={D} call {rep}")
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"call {rep}: out differs from split"
+        assert torch.equal(lse, ref_lse), f"call {rep}: lse differs from split"
+
+
+@pytest.mark.parametrize("cfg", ["joint-16k", "mixres-4req", "edit-cfg-4seq"])
+def test_packed_vt_equals_split_full_size(cfg):
+    """The step's fused path at full size: V packed from its text and image
+    pieces straight into V^T in a workspace filled with 0xFF bytes (NaN V,
+    counters at -1), then the attention that reads it, twice: out and lse
+    equal, bit for bit, the flat pack + varlen_attn_fwd_split."""
+    log(f"[packed vt] {cfg}: generating inputs")
+    inp = wl.make_varlen_inputs(wl.WORKLOADS[cfg], torch.bfloat16)
+    res = _pipeline(inp)
+    H, D, T, R = inp.spec.H, inp.spec.D, inp.total_tokens, inp.R
+    mask_d = torch.from_numpy(inp.text_mask.astype(np.uint8)).to(DEV)
+    hw_d = torch.tensor(inp.img_hw, dtype=torch.int32, device=DEV).reshape(-1, 2)
+    cu_j, cu_t, cu_i, img_dst = vl.joint_cu_seqlens(mask_d, hw_d)
+    ws = torch.full((vl.varlen_split_workspace_bytes(T, R, H, D),), 0xFF, dtype=torch.uint8, device=DEV)
+    vl.pack_v_transposed([(inp.v_text.to(DEV), cu_t, cu_j[:-1]), (inp.v_img.to(DEV), cu_i, img_dst)], cu_j, T, ws)
+    for rep in range(2):
+        out = torch.full_like(res["out"], float("nan"))
+        lse = torch.full_like(res["lse"], float("nan"))
+        vl.varlen_attn_fwd_vt(res["q"], res["k"], cu_j, cu_j, inp.max_len, inp.max_len, ws, inp.scale,
+                              out=out, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), res["out"].view(torch.int16)), f"call {rep}: out differs"
+        assert torch.equal(lse, res["lse"]), f"call {rep}: lse differs"
+    del res, ws, out, lse
+    torch.cuda.empty_cache()
+
+
 def test_queue_launches_on_two_streams_do_not_interfere():
     """Two workspace launches in flight at once on two streams, each with its
     own workspace (its own queue counters) and its own batch: each result

@@ -108,6 +108,29 @@ def test_bad_scalars_rejected_before_launch(lib):
         == VL_EINVAL
     assert lib.varlen_attn_fwd_split(p, p, p, p, p, 8, 8, 1, 2, 128, 0.1, p, None, 9_000_000, p, 1 << 40, None) \
         == VL_EUNSUPPORTED
+    # V packed straight into V^T, and the attention that reads it: piece
+    # count, descriptor rows and requests, head_dim, workspace
+    vd = (vl._CopyDesc * 9)()
+    for i in range(9):
+        vd[i] = vl._CopyDesc(16, None, 16, None, 4, 2 * 64 * 2, 1, 0)  # H = 2, D = 64 rows, one request
+    vp = ctypes.cast(vd, ctypes.c_void_p)
+    assert lib.pack_v_transposed(vp, 0, p, 1, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL
+    assert lib.pack_v_transposed(vp, 9, p, 1, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL
+    assert lib.pack_v_transposed(None, 1, p, 1, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL
+    assert lib.pack_v_transposed(vp, 1, p, 1, 2, 96, 8, p, 1 << 20, None) == VL_EUNSUPPORTED
+    assert lib.pack_v_transposed(vp, 1, p, 1, 4, 64, 8, p, 1 << 20, None) == VL_EINVAL   # rows of H = 2, not 4
+    assert lib.pack_v_transposed(vp, 1, p, 2, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL   # descriptor has 1 request
+    assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, -1, p, 1 << 20, None) == VL_EINVAL
+    assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, 8, p, 16, None) == VL_EINVAL         # short workspace
+    assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, 8, None, 1 << 20, None) == VL_EINVAL
+    vd[0] = vl._CopyDesc(24, None, 16, None, 4, 2 * 64 * 2, 1, 0)                        # misaligned source
+    assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL
+    vd[0] = vl._CopyDesc(16, None, 16, None, 4, 2 * 64 * 2, 0, 0)                        # no requests: nothing to do
+    assert lib.pack_v_transposed(vp, 1, p, 0, 2, 64, 0, p, 0, None) == VL_OK
+    assert lib.varlen_attn_fwd_vt(p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, 8, p, 16, None) == VL_EINVAL
+    assert lib.varlen_attn_fwd_vt(p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, 8, None, 1 << 20, None) == VL_EINVAL
+    assert lib.varlen_attn_fwd_vt(p, p, p, p, 8, 8, 1, 2, 96, 0.1, p, None, 8, p, 1 << 20, None) == VL_EUNSUPPORTED
+    assert lib.varlen_attn_fwd_vt(None, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, 8, p, 1 << 20, None) == VL_EINVAL
     assert lib.varlen_split_workspace_bytes(8, 1, 2, 96, p) == VL_EUNSUPPORTED
     assert lib.varlen_split_workspace_bytes(8, 1, 2, 64, None) == VL_EINVAL
     assert lib.varlen_split_workspace_bytes(-1, 1, 2, 64, p) == VL_EINVAL
