@@ -2197,8 +2197,9 @@ int pack_v_transposed(const vl_copy_desc* descs, int32_t count, const int32_t* k
   vl::PackVtArgs a{};
   for (int i = 0; i < count; ++i) {
     const vl_copy_desc& d = descs[i];
-    if (!d.src || !d.cu_seqlens || !aligned16(d.src) || d.max_len < 0 || d.num_reqs != num_reqs ||
-        d.row_bytes != (int64_t)H * D * 2)
+    // a piece of no rows (max_len 0) may have a null source: it is never read
+    if ((!d.src && d.max_len > 0) || !d.cu_seqlens || !aligned16(d.src) || d.max_len < 0 ||
+        d.num_reqs != num_reqs || d.row_bytes != (int64_t)H * D * 2)
       return VL_EINVAL;
     a.piece[i] = vl::VtPiece{d.src, d.cu_seqlens, d.row_offsets, d.max_len};
   }

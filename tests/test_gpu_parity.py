@@ -518,7 +518,8 @@ def test_packed_vt_pieces_and_gaps_vs_oracle(D):
     """V packed from two padded pieces straight into V^T (pack_v_transposed)
     and attended through it (varlen_attn_fwd_vt), q != kv: keys no piece
     covers read as zero V (a gap inside request 0, a trailing gap in request
-    2), a request without keys gives 0 / -inf.  Against the oracle on the V
+    2), a piece of no rows covers nothing, a request without keys gives
+    0 / -inf.  Against the oracle on the V
     those pieces pack, and bit for bit against varlen_attn_fwd_split on the
     same V packed flat."""
     H = 2
@@ -545,7 +546,10 @@ def test_packed_vt_pieces_and_gaps_vs_oracle(D):
     i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32), device=DEV)
     T = int(kv_cu[-1])
     ws = torch.full((vl.varlen_split_workspace_bytes(T, R, H, D),), 0xFF, dtype=torch.uint8, device=DEV)
+    # plus a piece of no rows (an all-text batch's image buffer): it covers nothing
+    empty = torch.empty((R, 0, H, D), dtype=torch.bfloat16, device=DEV)
     vl.pack_v_transposed([(slab_a.to(DEV), i32(oracle.cu_seqlens_from_lengths(a_len)), i32(kv_cu[:-1])),
+                          (empty, i32([0] * (R + 1)), i32(kv_cu[:-1])),
                           (slab_b.to(DEV), i32(oracle.cu_seqlens_from_lengths(b_len)),
                            i32(np.asarray(kv_cu[:-1]) + np.asarray(a_len) + np.asarray(gap)))],
                          i32(kv_cu), T, ws)

@@ -125,6 +125,8 @@ def test_bad_scalars_rejected_before_launch(lib):
     assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, 8, None, 1 << 20, None) == VL_EINVAL
     vd[0] = vl._CopyDesc(24, None, 16, None, 4, 2 * 64 * 2, 1, 0)                        # misaligned source
     assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL
+    vd[0] = vl._CopyDesc(None, None, 16, None, 4, 2 * 64 * 2, 1, 0)                      # null source with rows
+    assert lib.pack_v_transposed(vp, 1, p, 1, 2, 64, 8, p, 1 << 20, None) == VL_EINVAL
     vd[0] = vl._CopyDesc(16, None, 16, None, 4, 2 * 64 * 2, 0, 0)                        # no requests: nothing to do
     assert lib.pack_v_transposed(vp, 1, p, 0, 2, 64, 0, p, 0, None) == VL_OK
     assert lib.varlen_attn_fwd_vt(p, p, p, p, 8, 8, 1, 2, 64, 0.1, p, None, 8, p, 16, None) == VL_EINVAL
