@@ -420,6 +420,8 @@ def pack_v_transposed(items, kv_cu_seqlens, kv_rows: int, workspace, stream=None
         _gpu(cu, "cu_seqlens", torch.int32)
         if offs is not None:
             _gpu(offs, "flat_row_offsets", torch.int32)
+            if offs.numel() < R:
+                raise VarlenError("flat_row_offsets must have one entry per request")
         if src.dim() != 4 or src.shape[0] != R or cu.numel() != R + 1:
             raise VarlenError("src_padded must be [num_reqs, max_len, H, D] and cu_seqlens [num_reqs + 1]")
         if row is not None and tuple(src.shape[2:]) != row:
