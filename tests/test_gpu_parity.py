@@ -462,7 +462,9 @@ VL_RANDOM = _varlen_random_cases(91, 10)
 def test_varlen_random_batches(case):
     """Each random batch through the three launches (bf16, bf16 with the
     workspace: staged V^T and the key split of the last round, fp32), every
-    output row and lse against the oracle, canaries around both."""
+    output row and lse against the oracle, canaries around both; the
+    workspace launch once more on V packed straight into V^T from a padded
+    per-request buffer, bit for bit."""
     ql, kl, H, D = case
     log(f"[varlen] random ql={ql} kl={kl} H={H} D={D}")
     q_cu = oracle.cu_seqlens_from_lengths(ql)
@@ -476,6 +478,21 @@ def test_varlen_random_batches(case):
         what = f"random {case} {'f32' if f32 else 'bf16'}{' split' if split else ''}"
         check_close(to64(out), ro, f32, what)
         check_lse(to64(lse), rl, f32, what)
+        if split:
+            R = len(kl)
+            slab = torch.zeros((R, max(max(kl), 1), H, D), dtype=dtype)
+            for r in range(R):
+                slab[r, :kl[r]] = v[kv_cu[r]:kv_cu[r + 1]]
+            i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32), device=DEV)
+            ws = torch.empty(vl.varlen_split_workspace_bytes(sum(kl), R, H, D), dtype=torch.uint8, device=DEV)
+            vl.pack_v_transposed([(slab.to(DEV), i32(kv_cu), i32(kv_cu[:-1]))], i32(kv_cu), sum(kl), ws)
+            o2 = torch.empty_like(out)
+            l2 = torch.empty_like(lse)
+            vl.varlen_attn_fwd_vt(q.to(DEV), k.to(DEV), i32(q_cu), i32(kv_cu), int(max(ql)), int(max(kl)), ws, scale,
+                                  out=o2, lse=l2)
+            torch.cuda.synchronize()
+            assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"{what}: packed V^T out differs"
+            assert torch.equal(l2, lse), f"{what}: packed V^T lse differs"
 
 
 # Request lengths of the three full-size workloads' shapes (text + image rows).
