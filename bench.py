@@ -256,6 +256,11 @@ class VarlenStep:
         self.vl.pack_by_cu_seqlens_batched(self.pack_qk_items)
         self.vl.pack_v_transposed(self.pack_v_items, self.cu_j, self.T, self.workspace)
 
+    def attention_split(self):
+        q, k, v = self.packed
+        self.vl.varlen_attn_fwd_split(q, k, v, self.cu_j, self.cu_j, self.max_len, self.max_len, self.inp.scale,
+                                      out=self.out, workspace=self.workspace)
+
     def attention(self):
         q, k, _ = self.packed
         self.vl.varlen_attn_fwd_vt(q, k, self.cu_j, self.cu_j, self.max_len, self.max_len, self.workspace,
@@ -401,6 +406,29 @@ def main():
     traffic = load_traffic(args.workload)
 
     if not args.no_detail:
+        # the same step with the flat pack of all six pieces and the V^T
+        # staging inside the attention call (varlen_attn_fwd_split): what
+        # packing V straight into V^T saves, on this machine, the two forms
+        # timed in alternating rounds so that clock drift hits both alike
+        unfused = [(None, main_step.cu), ("pack", main_step.pack_flat), ("attn", main_step.attention_split),
+                   ("unpack", main_step.unpack), ("blocal", block_local_all)]
+        per = max(2, args.steps // 4)
+        acc = {"fused": [], "unfused": []}
+        for _ in range(4):
+            for tag, pp_ in (("fused", parts), ("unfused", unfused)):
+                rdt, rms = time_steps(stream, pp_, per, 1)
+                acc[tag].append((rdt * 1e3 / per, rms["pack"] * 1e3, rms["attn"]))
+        fused_ms = float(np.median([x[0] for x in acc["fused"]]))
+        unf = [float(np.median([x[i] for x in acc["unfused"]])) for i in range(3)]
+        detail["step_flat_pack_and_staging_call"] = {
+            "rounds": 4, "steps_per_round": per, "step_ms": round(unf[0], 4), "pack_us": round(unf[1], 2),
+            "attention_ms": round(unf[2], 4),
+            "attention_pct_of_bf16_peak": round(100 * flop_varlen / (unf[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+            "fused_step_ms_same_rounds": round(fused_ms, 4),
+            "step_ms_saved_by_the_fused_pack": round(unf[0] - fused_ms, 4)}
+        err(f"[bench] same step with the flat pack and the staging call: "
+            f"{detail['step_flat_pack_and_staging_call']['step_ms']} ms "
+            f"(fused V^T pack saves {detail['step_flat_pack_and_staging_call']['step_ms_saved_by_the_fused_pack']} ms)")
         flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
         def call_stats(fn, flushed: bool, reps: int = 50, warm: int = 10):
