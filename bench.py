@@ -42,6 +42,7 @@ import hashlib
 import json
 import multiprocessing as mp
 import os
+import re
 import sys
 import time
 
@@ -61,10 +62,17 @@ def err(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention sources (attn.hip, vl_device.h) with comments and
+    blank lines removed: a change of code changes it, a change of comments
+    does not."""
     h = hashlib.sha256()
     for name in ("attn.hip", "vl_device.h"):
-        with open(os.path.join(HERE, "packed_variable_length_varlen_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, "packed_variable_length_varlen_amd", "csrc", name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*$", "", line).rstrip()
+            if code.strip():
+                h.update((code + "\n").encode())
     return h.hexdigest()[:16]
 
 

@@ -12,9 +12,11 @@
 //    one wave issues MFMAs while the other does the softmax; K/V tiles rotate
 //    through three LDS buffers.  With a caller workspace, vt_transpose_kernel
 //    first stages V as V^T (the MFMA's V operand then is a plain 16-byte LDS
-//    read) and the last, partial round of tiles is cut along the keys, its
-//    parts combined by split_merge_kernel; without one, V tiles are read
-//    row-major with transposing LDS reads.
+//    read; pack_vt_kernel writes the same V^T straight from the padded V
+//    pieces, so the pack and the staging are one pass), the work items are
+//    taken through per-chiplet queues, and the last, partial round of tiles
+//    is cut along the keys, its parts combined by split_merge_kernel;
+//    without one, V tiles are read row-major with transposing LDS reads.
 //  * block_local_bf16_kernel / block_local_f32_kernel (block-local, D = 64,
 //    blocks of <= 32 frames): one wave per query block of one (batch, head),
 //    its window in 32-key chunks, V copied straight to LDS.
