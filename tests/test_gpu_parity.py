@@ -404,8 +404,9 @@ def test_varlen_check_cu_seqlens_option():
 
 
 def test_varlen_invariants_bitwise():
-    """Alone == inside the packed batch, permutation permutes outputs, and two
-    runs give the same bits (the tiles never mix requests)."""
+    """Alone == inside the packed batch, permutation permutes outputs, two
+    identical requests give identical outputs, and two runs give the same
+    bits (the tiles never mix requests)."""
     log("[varlen] invariants")
     ql = [300, 77, 1000, 129]
     H, D = 3, 128
@@ -426,6 +427,12 @@ def test_varlen_invariants_bitwise():
     op, _ = _run_varlen(qp, kp, vp, cup, cup, 0.1, False)
     for i, r in enumerate(perm):
         assert torch.equal(op[int(cup[i]):int(cup[i + 1])], out[int(cu[r]):int(cu[r + 1])])
+    # two identical requests in one batch give identical outputs
+    sl = slice(int(cu[0]), int(cu[1]))
+    qd, kd, vd = (torch.cat([t[sl], t[sl]]) for t in (q, k, v))
+    cud = [0, ql[0], 2 * ql[0]]
+    od, ld = _run_varlen(qd, kd, vd, cud, cud, 0.1, False)
+    assert torch.equal(od[:ql[0]], od[ql[0]:]) and torch.equal(ld[:ql[0]], ld[ql[0]:])
 
 
 # ------------------------------------------------------------------ key split of the last round
