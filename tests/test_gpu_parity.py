@@ -677,6 +677,18 @@ def test_varlen_split_vs_oracle(name, ql, kl, H, D):
     ro, rl = oracle.varlen_attention(to64(q), to64(k), to64(v), q_cu, kv_cu, scale)
     check_close(to64(out), ro, False, name)
     check_lse(to64(lse), rl, False, name)
+    # the same launch on V packed straight into V^T from a padded buffer: the same bits
+    R = len(kl)
+    slab = torch.zeros((R, max(max(kl), 1), H, D), dtype=torch.bfloat16)
+    for r in range(R):
+        slab[r, :kl[r]] = v[kv_cu[r]:kv_cu[r + 1]]
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32), device=DEV)
+    ws = torch.empty(vl.varlen_split_workspace_bytes(int(kv_cu[-1]), R, H, D), dtype=torch.uint8, device=DEV)
+    vl.pack_v_transposed([(slab.to(DEV), i32(kv_cu), None)], i32(kv_cu), int(kv_cu[-1]), ws)
+    ov, lv = vl.varlen_attn_fwd_vt(q.to(DEV), k.to(DEV), i32(q_cu), i32(kv_cu), max(ql), max(kl), ws, scale,
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ov.view(torch.int16), out.view(torch.int16)) and torch.equal(lv, lse), f"{name}: packed V^T"
     # against the unsplit launch: the same math up to fp32 summation order
     o1, l1 = _run_varlen(q, k, v, q_cu, kv_cu, scale, False)
     assert (o1.float() - out.float()).abs().max().item() <= 2 ** -7
