@@ -781,7 +781,9 @@ def _pipeline(inp):
     vl.pack_by_cu_seqlens_batched(items)
     q, k, v = packed
     max_len = inp.max_len
-    # bf16 runs the launch the benchmark times (key split of the last round)
+    # bf16 runs the workspace launch (V^T staging, key split of the last round,
+    # chiplet queues); test_packed_vt_equals_split_full_size checks that the
+    # benchmarked form, on V packed straight into V^T, gives the same bits
     fn = vl.varlen_attn_fwd_f32 if inp.dtype == torch.float32 else vl.varlen_attn_fwd_split
     out, lse = fn(q, k, v, cu_j, cu_j, max_len, max_len, inp.scale, return_lse=True)
     out_txt = torch.empty_like(inp.q_text, device=DEV)
