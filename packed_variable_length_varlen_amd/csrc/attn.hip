@@ -1476,8 +1476,12 @@ __global__ void __launch_bounds__(64 * kBlockWaves, 3) block_local_f32_kernel(At
     st.softmax_tile(s, a.c);
     // this chunk's V copy has landed
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // step j contracts keys 8(j/4) + j%4 (lane half 0) and 4 more (half 1):
+    // steps whose lower key is past the chunk's last key multiply P = 0
+    const int kv = min(32, u.k_hi - key0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
+      if (8 * (j >> 2) + (j & 3) >= kv) continue;
       const int rowoff = (8 * (j >> 2) + (j & 3)) * 256;
       const float v0 = *(const float*)(vbuf + rowoff + vrd0);
       const float v1 = *(const float*)(vbuf + rowoff + vrd1);
