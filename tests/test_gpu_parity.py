@@ -589,6 +589,42 @@ def test_packed_vt_pieces_and_gaps_vs_oracle(D):
         assert torch.equal(lse, ref_lse), f"call {rep}: lse differs from split"
 
 
+def test_packed_vt_overlapping_pieces_first_wins():
+    """Where two pieces cover the same key, the first one given supplies it:
+    piece A covers every key, piece B (listed second) the middle of each
+    request with other values, and the result equals the split launch on
+    piece A's V alone, bit for bit; listed the other way round, the middle
+    keys come from B."""
+    H, D = 2, 64
+    kl = [100, 37]
+    R = len(kl)
+    kv_cu = oracle.cu_seqlens_from_lengths(kl)
+    rng = np.random.default_rng(77)
+    bf = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    q, k = bf(int(kv_cu[-1]), H, D), bf(int(kv_cu[-1]), H, D)
+    slab_a, slab_b = bf(R, max(kl), H, D), bf(R, 20, H, D)
+    b_len, b_at = [20, 10], [30, 5]                 # piece B: keys b_at .. b_at + b_len of each request
+    i32 = lambda x: torch.tensor(np.asarray(x, dtype=np.int32), device=DEV)
+    piece_a = (slab_a.to(DEV), i32(kv_cu), i32(kv_cu[:-1]))
+    piece_b = (slab_b.to(DEV), i32(oracle.cu_seqlens_from_lengths(b_len)), i32(np.asarray(kv_cu[:-1]) + b_at))
+    T = int(kv_cu[-1])
+    scale = wl.softmax_scale(D)
+    for order in ("ab", "ba"):
+        v_flat = torch.zeros((T, H, D), dtype=torch.bfloat16)
+        for r in range(R):
+            v_flat[kv_cu[r]:kv_cu[r + 1]] = slab_a[r, :kl[r]]
+            if order == "ba":
+                v_flat[kv_cu[r] + b_at[r]:kv_cu[r] + b_at[r] + b_len[r]] = slab_b[r, :b_len[r]]
+        ref_out, ref_lse = _run_varlen(q, k, v_flat, kv_cu, kv_cu, scale, False, split=True)
+        ws = torch.empty(vl.varlen_split_workspace_bytes(T, R, H, D), dtype=torch.uint8, device=DEV)
+        vl.pack_v_transposed([piece_a, piece_b] if order == "ab" else [piece_b, piece_a], i32(kv_cu), T, ws)
+        out, lse = vl.varlen_attn_fwd_vt(q.to(DEV), k.to(DEV), i32(kv_cu), i32(kv_cu), max(kl), max(kl), ws, scale,
+                                         return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"order {order}: out differs"
+        assert torch.equal(lse, ref_lse), f"order {order}: lse differs"
+
+
 @pytest.mark.parametrize("cfg", ["joint-16k", "mixres-4req", "edit-cfg-4seq"])
 def test_packed_vt_equals_split_full_size(cfg):
     """The step's fused path at full size: V packed from its text and image
